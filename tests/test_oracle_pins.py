@@ -1,0 +1,484 @@
+"""Pins for the FP64 oracle: values fixed by the pages and by mathematics.
+
+Each pin is a function of the oracle module so that the planted-mistake tests
+at the end can re-run it against a deliberately broken oracle (monkeypatched on
+the CPU) and show it goes red.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as OA
+from oracle import brute
+from workloads import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _mask_prefill(q, k, v, mask, *, scale, softcap=0.0, alibi=None, q_pos=None, causal=False,
+                  dtype="f32"):
+    return oracle.prefill(q=q, k=k, v=v, kv_dtype=dtype, scale=scale, softcap=softcap,
+                          alibi=alibi, q_pos=q_pos, mask=mask, causal=causal)
+
+
+def _sel_prefill(q, k, v, sel, *, scale, block_size=1, softcap=0.0, alibi=None, q_pos=None,
+                 dtype="f32"):
+    return oracle.prefill(q=q, k=k, v=v, kv_dtype=dtype, scale=scale, softcap=softcap,
+                          alibi=alibi, q_pos=q_pos, sel=sel, block_size=block_size)
+
+
+# ----------------------------------------------------------------------------
+# pins written from the pages' examples
+# ----------------------------------------------------------------------------
+
+def pin_m03_excluded_row():
+    g = _load("m03_excluded_row.json")
+    q = np.array(g["q"], np.float32)[0].transpose(1, 0, 2)       # [rows][heads][D]
+    k = np.array(g["k"], np.float32)[0].transpose(1, 0, 2)       # [keys][kvheads][D]
+    v = np.full_like(k, g["v_fill"])
+    mask = np.array([[float(x) for x in row] for row in g["bias"]], np.float32)
+    out = _mask_prefill(q, k, v, mask, scale=g["scale"])
+    exp = np.array(g["expected"], np.float64)[0].transpose(1, 0, 2)
+    assert np.array_equal(out, exp), out
+    assert not np.signbit(out).any(), "excluded row must be +0.0"
+
+
+def pin_softcap_before_alibi():
+    g = _load("softcap_alibi_order.json")
+    q = np.array([[[1.0]]], np.float32)
+    k = np.zeros((29, 1, 1), np.float32)
+    v = np.zeros((29, 1, 1), np.float32)
+    k[0, 0, 0] = 60.0
+    v[0, 0, 0] = 1.0
+    sel = np.array([[0, 28]], np.int32)
+    out = _sel_prefill(q, k, v, sel, scale=1.0, softcap=30.0,
+                       alibi=np.array([1.0], np.float32), q_pos=np.array([28], np.int32))
+    assert abs(out[0, 0, 0] - g["expected_output"]) < 1e-14, out
+    # independent closed form, worked by hand
+    s_a = 30.0 * math.tanh(2.0) - 28.0
+    assert abs(out[0, 0, 0] - 1.0 / (1.0 + math.exp(-s_a))) < 1e-14
+
+
+def pin_bias_range():
+    g = _load("bias_range.json")
+    D = 3
+    q = np.ones((1, 1, D), np.float32)
+    k = np.zeros((2, 1, D), np.float32)
+    v = np.stack([np.zeros((1, D)), np.ones((1, D))]).astype(np.float32)
+    mask = np.array([[100000.0, 100001.0]], np.float32)
+    out = _mask_prefill(q, k, v, mask, scale=1.0)
+    assert np.allclose(out, g["expected_output"], rtol=0, atol=1e-15), out
+    assert abs(out[0, 0, 0] - math.e / (1.0 + math.e)) < 1e-15
+
+
+def pin_finite_sentinel():
+    # nonzero dots (the review's point that tests only produced zero scores)
+    rng = np.random.default_rng(7)
+    for sentinel in (-1e30, -np.finfo(np.float32).max):
+        q = rng.standard_normal((1, 2, 8)).astype(np.float32)
+        k = rng.standard_normal((5, 1, 8)).astype(np.float32)
+        v = rng.standard_normal((5, 1, 8)).astype(np.float32)
+        mask = np.full((1, 5), sentinel, np.float32)
+        out = _mask_prefill(q, k, v, mask, scale=0.5)
+        mean = v[:, 0].astype(np.float64).mean(axis=0)
+        assert np.allclose(out[0, 0], mean, rtol=1e-14, atol=1e-15)
+        assert np.allclose(out[0, 1], mean, rtol=1e-14, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# closed forms
+# ----------------------------------------------------------------------------
+
+def pin_one_key_returns_v():
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((1, 4, 16)).astype(np.float32)
+    k = rng.standard_normal((9, 2, 16)).astype(np.float32)
+    v = rng.standard_normal((9, 2, 16)).astype(np.float32)
+    out = _sel_prefill(q, k, v, np.array([[5]], np.int32), scale=0.25)
+    for h in range(4):
+        assert np.array_equal(out[0, h], v[5, h // 2].astype(np.float64))
+
+
+def pin_zero_query_mean():
+    rng = np.random.default_rng(12)
+    S, R, Hq, Hkv, D, cap = 2, 3, 4, 2, 8, 10
+    q = np.zeros((S, R, Hq, D), np.float32)
+    k = rng.standard_normal((S, cap, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((S, cap, Hkv, D)).astype(np.float32)
+    kv_len = np.array([7, 10], np.int32)
+    out = oracle.decode(q=q, k=k, v=v, kv_dtype="f32", kv_len=kv_len, causal=True, scale=1.0)
+    for b in range(S):
+        for r in range(R):
+            lim = kv_len[b] - R + r + 1
+            for h in range(Hq):
+                mean = v[b, :lim, h // 2].astype(np.float64).mean(axis=0)
+                assert np.allclose(out[b, r, h], mean, rtol=1e-13, atol=1e-15)
+
+
+def pin_two_key_logistic():
+    # scores a and b: weight of key 1 = 1 / (1 + exp(a - b))
+    q = np.array([[[1.0, 2.0]]], np.float32)
+    k = np.array([[[0.5, 0.25]], [[-1.0, 0.75]]], np.float32)
+    v = np.array([[[1.0, 0.0]], [[0.0, 1.0]]], np.float32)
+    out = _mask_prefill(q, k, v, np.zeros((1, 2), np.float32), scale=0.5)
+    a = 0.5 * (0.5 + 0.5)
+    b = 0.5 * (-1.0 + 1.5)
+    w1 = 1.0 / (1.0 + math.exp(a - b))
+    assert abs(out[0, 0, 1] - w1) < 1e-15 and abs(out[0, 0, 0] - (1 - w1)) < 1e-15
+
+
+def pin_weights_sum_to_one():
+    # V = 1 everywhere -> output 1 whatever the scores (sum of weights is 1)
+    wl = gen.make_prefill_mask(seed=3, n_row=5, n_head_q=4, n_head_kv=2, head_dim=8, n_kv=37,
+                               kv_dtype="f32", softcap=30.0, alibi=True)
+    v = np.ones_like(wl.v)
+    out = _mask_prefill(wl.q, wl.k, v, wl.mask, scale=wl.scale, softcap=30.0, alibi=wl.alibi,
+                        q_pos=wl.q_pos, causal=True)
+    assert np.allclose(out, 1.0, rtol=0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# reductions to library routines
+# ----------------------------------------------------------------------------
+
+def pin_scipy_softmax_dense():
+    from scipy.special import softmax
+    wl = gen.make_decode(seed=21, n_stream=2, n_row=1, n_head_q=6, n_head_kv=3, head_dim=16,
+                         cap=40, kv_dtype="bf16", depths=[40, 23], causal=False)
+    out = oracle.decode(q=wl.q, k=wl.k, v=wl.v, kv_dtype="bf16", kv_len=wl.kv_len, causal=False,
+                        scale=wl.scale)
+    for b in range(2):
+        n = wl.kv_len[b]
+        k64 = (wl.k[b, :n].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        v64 = (wl.v[b, :n].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        for h in range(6):
+            s = wl.scale * (k64[:, h // 2] @ wl.q[b, 0, h].astype(np.float64))
+            ref = softmax(s) @ v64[:, h // 2]
+            assert np.allclose(out[b, 0, h], ref, rtol=1e-12, atol=1e-14)
+
+
+def pin_torch_sdpa_mask_alibi_gqa():
+    import torch
+    wl = gen.make_prefill_mask(seed=22, n_row=6, n_head_q=8, n_head_kv=2, head_dim=16, n_kv=50,
+                               kv_dtype="f16", causal=True, alibi=True)
+    out = _mask_prefill(wl.q, wl.k, wl.v, wl.mask, scale=wl.scale, alibi=wl.alibi,
+                        q_pos=wl.q_pos, causal=True, dtype="f16")
+    q = torch.from_numpy(wl.q.astype(np.float64)).permute(1, 0, 2)[None]          # [1,H,R,D]
+    k = torch.from_numpy(wl.k.astype(np.float64)).permute(1, 0, 2)
+    v = torch.from_numpy(wl.v.astype(np.float64)).permute(1, 0, 2)
+    k = k.repeat_interleave(4, dim=0)[None].contiguous()
+    v = v.repeat_interleave(4, dim=0)[None].contiguous()
+    j = np.arange(50)[None, :]
+    bias = np.empty((8, 6, 50))
+    for h in range(8):
+        bias[h] = wl.mask.astype(np.float64) + wl.alibi[h] * (j - wl.q_pos[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, attn_mask=torch.from_numpy(bias)[None], scale=wl.scale)[0].permute(1, 0, 2).numpy()
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# invariances
+# ----------------------------------------------------------------------------
+
+def pin_split_equals_unsplit():
+    wl = gen.make_decode(seed=31, n_stream=3, n_row=4, n_head_q=4, n_head_kv=2, head_dim=8,
+                         cap=21, kv_dtype="i8", depths=[21, 9, 4], causal=True, softcap=5.0,
+                         alibi=True)
+    kw = dict(q=wl.q, k=wl.k, v=wl.v, kv_dtype="i8", kv_len=wl.kv_len, causal=True,
+              scale=wl.scale, softcap=5.0, alibi=wl.alibi, k_scale=wl.k_scale, v_scale=wl.v_scale)
+    ref = oracle.decode(**kw)
+    for L in range(1, 23):
+        out, po, pm, pl = oracle.decode_split(slice_len=L, **kw)
+        err = np.abs(out - ref).max() / np.abs(ref).max()
+        assert err < 1e-13, (L, err)
+
+
+def pin_split_prefill_equals_unsplit():
+    wl = gen.make_prefill_sel(seed=32, n_row=3, n_head_q=4, n_head_kv=1, head_dim=8, n_kv=40,
+                              kv_dtype="bf16", n_sel=9, n_dup=2, n_invalid=1, block_size=4)
+    kw = dict(q=wl.q, k=wl.k, v=wl.v, kv_dtype="bf16", scale=wl.scale, q_pos=wl.q_pos,
+              sel=wl.sel, block_size=4)
+    ref = oracle.prefill(**kw)
+    for n in (1, 2, 3, 7, 40):
+        out = oracle.prefill_split(n_splits=n, **kw)
+        assert np.allclose(out, ref, rtol=1e-13, atol=1e-15), n
+
+
+def pin_selection_invariances():
+    wl = gen.make_prefill_sel(seed=41, n_row=4, n_head_q=4, n_head_kv=2, head_dim=8, n_kv=30,
+                              kv_dtype="bf16", n_sel=8, n_dup=2, n_invalid=2, block_size=3)
+    kw = dict(q=wl.q, k=wl.k, v=wl.v, kv_dtype="bf16", scale=wl.scale, q_pos=wl.q_pos,
+              block_size=3)
+    ref = oracle.prefill(sel=wl.sel, **kw)
+    rng = np.random.default_rng(0)
+    perm = np.stack([row[rng.permutation(row.size)] for row in wl.sel])
+    assert np.array_equal(oracle.prefill(sel=perm, **kw), ref)
+    more = np.concatenate([wl.sel, wl.sel[:, :3], np.full((4, 2), -7, np.int32),
+                           np.full((4, 1), 10, np.int32)], axis=1)   # id 10: cells 30..32 >= N
+    assert np.array_equal(oracle.prefill(sel=more, **kw), ref)
+    # selection == dense mask mode with -inf outside the visible set
+    mask = np.full((4, 30), -np.inf, np.float32)
+    for r in range(4):
+        mask[r, oracle.visible_selection(wl.sel[r], 3, 30)] = 0.0
+    dense = oracle.prefill(mask=mask, **kw)
+    assert np.allclose(dense, ref, rtol=1e-14, atol=1e-16)
+    # an all-cells list equals plain attention
+    allc = np.tile(np.arange(10, dtype=np.int32), (4, 1))
+    plain = oracle.prefill(mask=np.zeros((4, 30), np.float32), **kw)
+    assert np.allclose(oracle.prefill(sel=allc, **kw), plain, rtol=1e-14, atol=1e-16)
+
+
+def pin_gqa_equals_mha():
+    wl = gen.make_decode(seed=51, n_stream=2, n_row=2, n_head_q=6, n_head_kv=2, head_dim=8,
+                         cap=12, kv_dtype="f16", depths=[12, 7], causal=True, alibi=False)
+    kw = dict(kv_dtype="f16", kv_len=wl.kv_len, causal=True, scale=wl.scale)
+    ref = oracle.decode(q=wl.q, k=wl.k, v=wl.v, **kw)
+    k_rep = np.repeat(wl.k, 3, axis=2)
+    v_rep = np.repeat(wl.v, 3, axis=2)
+    mha = oracle.decode(q=wl.q, k=k_rep, v=v_rep, **kw)
+    assert np.array_equal(ref, mha)
+
+
+# ----------------------------------------------------------------------------
+# NaN / infinity rules
+# ----------------------------------------------------------------------------
+
+def pin_nan_rules():
+    rng = np.random.default_rng(61)
+    D = 4
+    q = rng.standard_normal((1, 2, D)).astype(np.float32)
+    k = rng.standard_normal((6, 1, D)).astype(np.float32)
+    v = rng.standard_normal((6, 1, D)).astype(np.float32)
+    base_mask = np.zeros((1, 6), np.float32)
+    base_mask[0, 4:] = -np.inf
+    ref = _mask_prefill(q, k, v, base_mask, scale=0.5)
+    assert np.isfinite(ref).all()
+    # NaN in an excluded key / value: no effect
+    k2, v2 = k.copy(), v.copy()
+    k2[4:] = np.nan
+    v2[4:] = np.nan
+    assert np.array_equal(_mask_prefill(q, k2, v2, base_mask, scale=0.5), ref)
+    # NaN in a visible K element -> every head of that kv group is NaN
+    k3 = k.copy()
+    k3[1, 0, 2] = np.nan
+    assert np.isnan(_mask_prefill(q, k3, v, base_mask, scale=0.5)).all()
+    # NaN in one dim of a visible V -> only that dim is NaN
+    v3 = v.copy()
+    v3[2, 0, 1] = np.nan
+    o3 = _mask_prefill(q, k, v3, base_mask, scale=0.5)
+    assert np.isnan(o3[..., 1]).all() and np.isfinite(o3[..., [0, 2, 3]]).all()
+    # NaN in V where the weight underflows to 0 still poisons that dim
+    mask4 = base_mask.copy()
+    mask4[0, 3] = -1e4
+    v4 = v.copy()
+    v4[3, 0, 0] = np.nan
+    o4 = _mask_prefill(q, k, v4, mask4, scale=0.5)
+    assert np.isnan(o4[..., 0]).all() and np.isfinite(o4[..., 1:]).all()
+    # +inf score -> NaN row
+    mask5 = base_mask.copy()
+    mask5[0, 0] = np.inf
+    assert np.isnan(_mask_prefill(q, k, v, mask5, scale=0.5)).all()
+    # every visible score -inf -> +0.0
+    s = np.array([[-np.inf, -np.inf]])
+    o7 = OA.attend_scores(s, np.ones((2, 3)))
+    assert np.array_equal(o7, np.zeros((1, 3))) and not np.signbit(o7).any()
+
+
+def pin_combine_rules():
+    D = 3
+    o = np.array([[[1.0, 2.0, 3.0]], [[0.0, 0.0, 0.0]]])
+    m = np.array([[0.5], [-np.inf]])
+    l = np.array([[2.0], [0.0]])
+    assert np.allclose(OA.combine_partials(o, m, l), [[0.5, 1.0, 1.5]])
+    m_nan = np.array([[0.5], [np.nan]])
+    assert np.isnan(OA.combine_partials(o, m_nan, l)).all()
+    m_inf = np.array([[0.5], [np.inf]])
+    assert np.isnan(OA.combine_partials(o, m_inf, l)).all()
+    m_empty = np.array([[-np.inf], [-np.inf]])
+    z = OA.combine_partials(np.zeros_like(o), m_empty, np.zeros_like(l))
+    assert np.array_equal(z, np.zeros((1, D))) and not np.signbit(z).any()
+    # NaN carried in a partial's value vector survives the merge
+    o_nan = o.copy()
+    o_nan[0, 0, 1] = np.nan
+    c = OA.combine_partials(o_nan, m, l)
+    assert np.isnan(c[0, 1]) and np.isfinite(c[0, [0, 2]]).all()
+
+
+def pin_storage_decoding():
+    bits = np.array([0x3F80, 0xC000, 0x7F80, 0x0001, 0x3EAB], np.uint16)
+    got = OA.kv_to_f64(bits, "bf16")
+    assert got[0] == 1.0 and got[1] == -2.0 and got[2] == np.inf
+    assert got[3] == 2.0 ** -133 and got[4] == 0.333984375
+    assert OA.kv_to_f64(np.array([0x3C00], np.uint16).view(np.float16), "f16")[0] == 1.0
+    i8 = np.array([[-127, 0, 5]], np.int8)
+    sc = np.array([0.5], np.float32)
+    assert np.array_equal(OA.kv_to_f64(i8, "i8", sc), [[-63.5, 0.0, 2.5]])
+    # the generator's bf16 rounding: nearest, ties to even
+    x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9], np.float32)
+    assert list(gen.f32_to_bf16_bits(x)) == [0x3F80, 0x3F82, 0x3F80]
+
+
+# ----------------------------------------------------------------------------
+# the scalar twin
+# ----------------------------------------------------------------------------
+
+def _close_with_pattern(a, b, tol):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    fin = np.isfinite(b)
+    assert np.array_equal(a[~fin & ~np.isnan(b)], b[~fin & ~np.isnan(b)])
+    z = b == 0
+    assert np.array_equal(a[z], b[z])
+    if fin.any():
+        assert np.abs(a[fin] - b[fin]).max() <= tol * max(1.0, np.abs(b[fin]).max())
+
+
+def pin_brute_decode():
+    for i, dt in enumerate(("f32", "f16", "bf16", "i8")):
+        wl = gen.make_decode(seed=100 + i, n_stream=2, n_row=3, n_head_q=4, n_head_kv=2,
+                             head_dim=4, cap=9, kv_dtype=dt, depths=[9, 2], causal=(i % 2 == 0),
+                             softcap=(3.0 if i >= 2 else 0.0), alibi=(i % 2 == 1))
+        kw = dict(q=wl.q, k=wl.k, v=wl.v, kv_dtype=dt, kv_len=wl.kv_len, causal=wl.causal,
+                  scale=wl.scale, softcap=wl.softcap, alibi=wl.alibi, k_scale=wl.k_scale,
+                  v_scale=wl.v_scale)
+        _close_with_pattern(oracle.decode(**kw), brute.decode(**kw), 1e-13)
+
+
+def pin_brute_prefill():
+    wl = gen.make_prefill_mask(seed=120, n_row=4, n_head_q=4, n_head_kv=2, head_dim=4, n_kv=9,
+                               kv_dtype="bf16", excluded_rows=1, nan_k=2, softcap=30.0, alibi=True)
+    kw = dict(q=wl.q, k=wl.k, v=wl.v, kv_dtype="bf16", scale=wl.scale, softcap=30.0,
+              alibi=wl.alibi, q_pos=wl.q_pos, mask=wl.mask, causal=True)
+    _close_with_pattern(oracle.prefill(**kw), brute.prefill(**kw), 1e-13)
+    wl = gen.make_prefill_sel(seed=121, n_row=3, n_head_q=2, n_head_kv=1, head_dim=4, n_kv=11,
+                              kv_dtype="f16", n_sel=5, n_dup=1, n_invalid=1, block_size=2,
+                              alibi=True)
+    kw = dict(q=wl.q, k=wl.k, v=wl.v, kv_dtype="f16", scale=wl.scale, alibi=wl.alibi,
+              q_pos=wl.q_pos, sel=wl.sel, block_size=2)
+    _close_with_pattern(oracle.prefill(**kw), brute.prefill(**kw), 1e-13)
+
+
+def pin_visited_sets():
+    st = oracle.visited_decode(kv_len=np.array([5, 3]), n_row=2, causal=True, slice_len=2,
+                               n_head_kv=1)
+    # stream 0: row 0 sees 0..3, row 1 sees 0..4; slices [0,2) [2,4) [4,6)
+    assert st[0, 0, 0].tolist() == [[2, 1, 1], [2, 5, 13], [0, 0, 0]]
+    assert st[0, 1, 0].tolist() == [[2, 1, 1], [2, 5, 13], [1, 4, 16]]
+    assert st[1, 1, 0].tolist() == [[2, 1, 1], [1, 2, 4], [0, 0, 0]]
+    cells, ids = oracle.visited_prefill(n_kv=10, n_head_kv=1,
+                                        sel=np.array([[4, -1, 1, 4, 2, 9]]), block_size=3)
+    assert ids[0].tolist() == [1, 2] and cells[0].tolist() == [3, 4, 5, 6, 7, 8]
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes in the oracle (CPU only): each must turn a pin red
+# ----------------------------------------------------------------------------
+
+def _expect_red(pin):
+    with pytest.raises(AssertionError):
+        pin()
+
+
+def test_planted_alibi_before_softcap(monkeypatch):
+    real = OA.scores
+
+    def swapped(q, kc, cells, *, scale, softcap=0.0, slopes=None, pos=0, mask_vals=None):
+        s = float(scale) * (np.asarray(q, np.float64) @ np.asarray(kc, np.float64).T)
+        if slopes is not None:
+            s = s + np.asarray(slopes, np.float64)[:, None] * (np.asarray(cells, np.float64) - pos)[None, :]
+        if softcap and softcap > 0:
+            s = softcap * np.tanh(s / softcap)
+        if mask_vals is not None:
+            s = s + np.asarray(mask_vals, np.float64)[None, :]
+        return s
+
+    monkeypatch.setattr(OA, "scores", swapped)
+    _expect_red(pin_softcap_before_alibi)
+    monkeypatch.setattr(OA, "scores", real)
+    pin_softcap_before_alibi()
+
+
+def test_planted_combine_nan_to_zero(monkeypatch):
+    real = OA.combine_partials
+
+    def lossy(o, m, l):
+        m = np.nan_to_num(np.asarray(m, np.float64), nan=-np.inf)
+        return np.nan_to_num(real(o, m, l), nan=0.0)
+
+    monkeypatch.setattr(OA, "combine_partials", lossy)
+    _expect_red(pin_combine_rules)
+
+
+def test_planted_no_dedup(monkeypatch):
+    def no_dedup(ids, block_size, n_kv):
+        ids = np.asarray(ids, dtype=np.int64)
+        ok = (ids >= 0) & (ids * block_size < n_kv)
+        blocks = np.sort(ids[ok])
+        cells = (blocks[:, None] * block_size + np.arange(block_size)[None, :]).reshape(-1)
+        return cells[cells < n_kv]
+
+    monkeypatch.setattr(OA, "visible_selection", no_dedup)
+    _expect_red(pin_selection_invariances)
+
+
+def test_planted_excluded_row_nan(monkeypatch):
+    real = OA.attend_scores
+
+    def nan_rows(s, vc):
+        out = real(s, vc)
+        s = np.asarray(s)
+        for h in range(s.shape[0]):
+            if s.shape[1] == 0 or np.all(s[h] == -np.inf):
+                out[h] = np.nan
+        return out
+
+    monkeypatch.setattr(OA, "attend_scores", nan_rows)
+    _expect_red(pin_m03_excluded_row)
+
+
+def test_planted_wrong_gqa_mapping(monkeypatch):
+    real = OA.decode
+
+    def modulo_heads(**kw):
+        q = kw["q"]
+        Hkv = kw["k"].shape[2]
+        G = q.shape[2] // Hkv
+        # planted: query head h reads kv head h % Hkv instead of h // G
+        order = np.array([(h % Hkv) * G + h // Hkv for h in range(q.shape[2])])
+        kw = dict(kw, q=q[:, :, order])
+        out = real(**kw)
+        inv = np.argsort(order)
+        return out[:, :, inv]
+
+    monkeypatch.setattr(oracle, "decode", modulo_heads)
+    _expect_red(pin_scipy_softmax_dense)
+
+
+def test_planted_dropped_scale(monkeypatch):
+    real = OA.scores
+
+    def unscaled(q, kc, cells, *, scale, **kw):
+        return real(q, kc, cells, scale=1.0, **kw)
+
+    monkeypatch.setattr(OA, "scores", unscaled)
+    _expect_red(pin_torch_sdpa_mask_alibi_gqa)
