@@ -1,0 +1,207 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--verify]
+
+One step = one split-K decode pass of the 16-stream workload (16 streams x 1
+query row, 32/4 heads, head dim 256, bf16 K/V, depths U[1024, 32768] drawn
+from seed, slices of 1024 keys): the decode kernel over every (stream, kv head,
+slice) followed by the log-sum-exp combine.  `value` is the decode K/V stream
+rate in GB/s (algorithmic bytes: every visible K and V row read once).
+
+The same run also times the maskless selected-key prefill (2048 rows at
+positions 30000..32047, 16/2 heads, head dim 256, bf16, 512 block ids per row
+over 4-cell blocks) and reports its TFLOP/s (4*D flops per visited (row, head,
+key)), and a plain device copy of 1 GiB (the achievable copy rate, and the
+calibration for the memory counters).  `--verify` adds the int8 verify-window
+decode (16 streams x 16 rows, 48/4 heads, depth 32000, slices of 2048).
+
+Prints ONE JSON line.  Inputs are seeded synthetic data (no dataset).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--verify", action="store_true", help="also time the int8 verify-window decode")
+    return ap.parse_args()
+
+
+def timed(fn, steps, torch):
+    """Average ms of `fn` over `steps` back-to-back calls, HIP events on the current stream."""
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline_decode(wl, streams):
+    """The FP64 oracle (as it stands) on a bounded sample of the decode workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    sl = slice(0, streams)
+    t0 = time.perf_counter()
+    oracle.decode(q=wl.q[sl], k=wl.k[sl], v=wl.v[sl], kv_dtype=wl.kv_dtype, kv_len=wl.kv_len[sl],
+                  causal=wl.causal, scale=wl.scale)
+    dt = time.perf_counter() - t0
+    cells = int(np.asarray(wl.kv_len[sl], np.int64).sum())
+    nbytes = cells * wl.n_head_kv * wl.head_dim * 2 * 2
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"split-K decode workload, streams 0..{streams - 1} ({cells} cells, all 32 heads), "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import split_flash_attention_amd as sa
+    from tests import hip_run
+    from workloads import gen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    sa.lib()
+
+    # ---- inputs (host generation, then resident in HBM) --------------------------
+    wl2 = gen.config2()
+    d2 = hip_run.DecodeDev(wl2, "cuda", poison_outputs=False)
+    a2 = d2.args()
+    c2 = d2.combine_args()
+    wl3 = gen.config3()
+    d3 = hip_run.PrefillDev(wl3, "cuda", poison_outputs=False)
+    a3 = d3.args()
+    copy_src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")     # 1 GiB
+    copy_dst = torch.empty_like(copy_src)
+    copy_src.fill_(1.0)
+
+    def step():
+        sa.sel_attn_decode(a2)
+        sa.sel_attn_split_combine(c2)
+
+    def decode_only():
+        sa.sel_attn_decode(a2)
+
+    def prefill():
+        sa.sel_attn_prefill(a3)
+
+    def copy():
+        copy_dst.copy_(copy_src)
+
+    for _ in range(args.warmup):
+        step()
+        prefill()
+        copy()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps -------------------------------------------
+    ms_step = timed(step, args.steps, torch)
+    ms_decode = timed(decode_only, args.steps, torch)
+    ms_prefill = timed(prefill, args.steps, torch)
+    ms_copy = timed(copy, max(3, args.steps // 4), torch)
+
+    cells = int(np.asarray(wl2.kv_len, np.int64).sum())
+    kv_bytes = cells * wl2.n_head_kv * wl2.head_dim * 2 * 2          # K and V, bf16
+    gbs_step = kv_bytes / (ms_step * 1e-3) / 1e9
+    gbs_kernel = kv_bytes / (ms_decode * 1e-3) / 1e9
+
+    # selected-key prefill work: 4*D flops per visited (row, query head, key)
+    n_cells = 0
+    for r in range(wl3.n_row):
+        ids = wl3.sel[r]
+        ok = (ids >= 0) & (ids.astype(np.int64) * wl3.block_size < wl3.n_kv)
+        n_cells += np.unique(ids[ok]).size * wl3.block_size
+    flops3 = 4.0 * wl3.head_dim * wl3.n_head_q * n_cells
+    gather3 = n_cells * wl3.n_head_kv * wl3.head_dim * 2 * 2
+    tflops3 = flops3 / (ms_prefill * 1e-3) / 1e12
+
+    result = {
+        "metric": "decode KV GB/s (% HBM peak) + sel-prefill TFLOP/s, GQA h256 at 32k depth",
+        "value": round(gbs_step, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, depths U[1024,32768])",
+        "config": {"workload": "split-K decode: 16 streams x 1 row, 32/4 heads, head dim 256, bf16 K/V, "
+                               "depths U[1024,32768], slices of 1024, LSE combine",
+                   "kv_bytes_per_step": kv_bytes, "decode_path": sa.decode_path(a2),
+                   "hbm_peak_frac_step": round(gbs_step / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs_kernel, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs_kernel / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode (mfma_attn_kernel, bf16, D=256)",
+                     "kernel_ms": round(ms_decode, 5)},
+        "sel_prefill": {"workload": "2048 rows x 512 block ids (4-cell blocks), 16/2 heads, D=256, bf16",
+                        "ms": round(ms_prefill, 5), "tflops": round(tflops3, 3),
+                        "mfma_peak_frac": round(tflops3 / BF16_PEAK_TFLOPS, 5),
+                        "gathered_gbs": round(gather3 / (ms_prefill * 1e-3) / 1e9, 2),
+                        "tokens_per_s": round(wl3.n_row / (ms_prefill * 1e-3), 1),
+                        "prefill_path": sa.prefill_path(a3)},
+        "copy_gbs": round(2 * copy_src.numel() * 4 / (ms_copy * 1e-3) / 1e9, 1),
+        "tokens_per_s": round(wl2.n_stream / (ms_step * 1e-3), 1),
+    }
+
+    if args.verify:
+        wl5 = gen.config5(32000)
+        d5 = hip_run.DecodeDev(wl5, "cuda", poison_outputs=False)
+        a5, c5 = d5.args(), d5.combine_args()
+
+        def step5():
+            sa.sel_attn_decode(a5)
+            sa.sel_attn_split_combine(c5)
+
+        step5()
+        ms5 = timed(step5, args.steps, torch)
+        cells5 = int(np.asarray(wl5.kv_len, np.int64).sum())
+        bytes5 = cells5 * wl5.n_head_kv * (wl5.head_dim + 4) * 2
+        flops5 = 0.0
+        for r in range(wl5.n_row):
+            flops5 += 4.0 * wl5.head_dim * wl5.n_head_q * wl5.n_stream * (int(wl5.kv_len[0]) - wl5.n_row + r + 1)
+        result["verify_decode"] = {"workload": "int8 verify: 16 streams x 16 rows, 48/4 heads, D=256, depth 32000",
+                                   "ms": round(ms5, 5), "gbs": round(bytes5 / (ms5 * 1e-3) / 1e9, 2),
+                                   "tflops": round(flops5 / (ms5 * 1e-3) / 1e12, 2)}
+        del d5
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_decode(wl2, streams=2)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

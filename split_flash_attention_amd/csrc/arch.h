@@ -1,0 +1,38 @@
+// gfx950 wave-level primitives used by the matrix-core kernels.
+//
+// v_mfma_f32_16x16x32_{bf16,f16} lane layout (wave64), as relied on below:
+//   A (16 x 32, rows m, contraction k): lane l holds A[l % 16][8 * (l / 16) + j], j = 0..7
+//   B (32 x 16, contraction k, cols n): lane l holds B[8 * (l / 16) + j][l % 16]
+//   C/D (16 x 16):                      lane l holds D[4 * (l / 16) + i][l % 16], i = 0..3
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace selattn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// D = A * B + C for 16x16x32 operands held as 8 packed 16-bit values per lane.
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (F16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+}
+
+// Butterfly exchange within the wave.
+__device__ __forceinline__ float wave_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
+__device__ __forceinline__ int wave_xor_i(int x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Wave-uniform "does any lane hold true".
+__device__ __forceinline__ bool wave_any(bool x) { return __any(x); }
+
+}  // namespace selattn

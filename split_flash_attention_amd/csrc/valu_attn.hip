@@ -1,0 +1,510 @@
+// Generic vector-ALU attention kernels: every storage type, every mode.
+//
+// One work-group owns up to 32 query vectors (a query vector is one (row,
+// query head) pair of one kv head) and walks a key range in tiles of 32 keys
+// with the online softmax of TensorFold PR #985 ("What this changes": a running
+// max per fixed key tile, the correction exp(m_old - m_new), l and o rescaled,
+// o / l at the end).  Tiles are fixed by key position, so results do not depend
+// on how the range is split among work-groups beyond the slice boundaries.
+//
+// Also here: the log-sum-exp merge of split partials (TensorFold PR #2595
+// attn_merge; strix-llama.cpp PR #115 split-K reduce) with NaN carried through
+// (HartsyInference PR #910, review item 1 and its fix).
+#include "common.h"
+#include "internal.h"
+
+#include <algorithm>
+
+namespace selattn {
+namespace {
+
+constexpr int kTile = 32;       // keys per tile
+constexpr int kQv = 32;         // query vectors per work-group
+constexpr int kThreads = 256;
+constexpr int kMaxD = 256;
+constexpr int kMaxSel = 4096;
+
+enum Mode : int { kDecode = 0, kMask = 1, kSel = 2 };
+
+struct ValuParams {
+    int mode;
+    int Hq, Hkv, G, D;
+    const float* q;
+    const void* k;
+    const void* v;
+    int dt;
+    int64_t kv_ss, kv_sc, kv_sh;
+    const float* ksc;
+    const float* vsc;
+    int64_t sc_ss, sc_sc, sc_sh;
+    float scale, softcap;
+    const float* alibi;
+    // decode
+    int S, R, cap;
+    const int32_t* kv_len;
+    int causal;
+    int slice_len, n_slices_max, n_qchunks;
+    // prefill
+    int n_kv;
+    const int32_t* q_pos;
+    const int32_t* sel;
+    int n_sel, bs, sel_pow2;
+    const float* mask;
+    int64_t m_sr, m_sh;
+    int rows_per_wg, n_splits, split_step;
+    // outputs
+    float* out;
+    float* part_o;
+    float* part_ml;
+    int64_t* dbg_visit;
+    int32_t* dbg_sel;
+};
+
+// LDS carve-up (bytes)
+constexpr int kOffQ = 0;                                         // float [kQv][kMaxD]
+constexpr int kOffK = kOffQ + kQv * kMaxD * 4;                   // float [kTile][kMaxD+1]
+constexpr int kOffV = kOffK + kTile * (kMaxD + 1) * 4;           // float [kTile][kMaxD]
+constexpr int kOffP = kOffV + kTile * kMaxD * 4;                 // float [kQv][kTile]
+constexpr int kOffList = kOffP + kQv * kTile * 4;                // int [kMaxSel]
+constexpr int kSmemBytes = kOffList + kMaxSel * 4;
+// the sort buffer reuses the V tile region (sorting ends before the first tile)
+static_assert(kTile * kMaxD * 4 >= kMaxSel * 4, "sort buffer must fit in the V tile");
+
+__global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
+    extern __shared__ __align__(16) char smem[];
+    float* qs = reinterpret_cast<float*>(smem + kOffQ);
+    float* kt = reinterpret_cast<float*>(smem + kOffK);
+    float* vt = reinterpret_cast<float*>(smem + kOffV);
+    float* ps = reinterpret_cast<float*>(smem + kOffP);
+    int* list = reinterpret_cast<int*>(smem + kOffList);
+    int* sortbuf = reinterpret_cast<int*>(smem + kOffV);
+
+    __shared__ int cell_t[kTile];
+    __shared__ uint32_t vis[kQv];
+    __shared__ float m_run[kQv], l_run[kQv], c_run[kQv];
+    __shared__ int nan_run[kQv];
+    __shared__ long long dbg[kQv][3];
+    __shared__ int scan[kThreads];
+    __shared__ int n_ids_s;
+
+    const int tid = threadIdx.x;
+    const int D = p.D;
+    const int G = p.G;
+    const int t_split = blockIdx.x;
+    const int g = blockIdx.y % p.Hkv;
+
+    // ---- work unit ------------------------------------------------------
+    int b = 0, m0 = 0, nq = 0, lo = 0, hi = 0, kvl = 0, row0 = 0;
+    if (p.mode == kDecode) {
+        b = blockIdx.z;
+        const int qc = blockIdx.y / p.Hkv;
+        kvl = min(max(p.kv_len[b], 0), p.cap);
+        lo = t_split * p.slice_len;
+        if (lo >= kvl) return;          // past this stream's slices: not written
+        hi = min(lo + p.slice_len, kvl);
+        m0 = qc * kQv;
+        nq = min(kQv, p.R * G - m0);
+        if (nq <= 0) return;
+    } else if (p.mode == kMask) {
+        row0 = blockIdx.z * p.rows_per_wg;
+        nq = min(p.rows_per_wg, p.R - row0) * G;
+        lo = t_split * p.split_step;
+        hi = min(lo + p.split_step, p.n_kv);
+    } else {
+        row0 = blockIdx.z;
+        nq = G;
+        lo = t_split * p.split_step;
+        hi = min(lo + p.split_step, p.n_kv);
+    }
+
+    // query vector i -> (row, head)
+    auto qrow = [&](int i) -> int {
+        return p.mode == kDecode ? (m0 + i) / G : row0 + i / G;
+    };
+    auto qhead = [&](int i) -> int {
+        return g * G + (p.mode == kDecode ? (m0 + i) % G : i % G);
+    };
+    auto qpos = [&](int i) -> int {
+        return p.mode == kDecode ? kvl - p.R + qrow(i) : (p.q_pos ? p.q_pos[qrow(i)] : 0);
+    };
+    auto qvec_ptr = [&](int i) -> const float* {
+        const int r = qrow(i), h = qhead(i);
+        if (p.mode == kDecode) return p.q + ((static_cast<int64_t>(b) * p.R + r) * p.Hq + h) * D;
+        return p.q + (static_cast<int64_t>(r) * p.Hq + h) * D;
+    };
+
+    // ---- load Q, init state ---------------------------------------------
+    for (int e = tid; e < nq * D; e += kThreads) {
+        const int i = e / D, d = e % D;
+        qs[i * kMaxD + d] = qvec_ptr(i)[d];
+    }
+    if (tid < kQv) {
+        m_run[tid] = kNegInf;
+        l_run[tid] = 0.f;
+        c_run[tid] = 0.f;
+        nan_run[tid] = 0;
+        dbg[tid][0] = dbg[tid][1] = dbg[tid][2] = 0;
+    }
+
+    // ---- selection list: sort, drop invalid and repeated ids --------------
+    int n_slots = hi - lo;
+    if (p.mode == kSel) {
+        const int P = p.sel_pow2;
+        const int32_t* srow = p.sel + static_cast<int64_t>(row0) * p.n_sel;
+        for (int e = tid; e < P; e += kThreads) {
+            int id = 0x7fffffff;
+            if (e < p.n_sel) {
+                const int x = srow[e];
+                if (x >= 0 && static_cast<int64_t>(x) * p.bs < p.n_kv) id = x;
+            }
+            sortbuf[e] = id;
+        }
+        __syncthreads();
+        for (int k = 2; k <= P; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int e = tid; e < P; e += kThreads) {
+                    const int o = e ^ j;
+                    if (o > e) {
+                        const int x = sortbuf[e], y = sortbuf[o];
+                        const bool up = (e & k) == 0;
+                        if ((x > y) == up) { sortbuf[e] = y; sortbuf[o] = x; }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        // stable compaction of the first occurrence of each valid id
+        const int per = (P + kThreads - 1) / kThreads;
+        const int e0 = tid * per;
+        int cnt = 0;
+        for (int e = e0; e < min(e0 + per, P); ++e) {
+            const int x = sortbuf[e];
+            cnt += (x != 0x7fffffff && (e == 0 || sortbuf[e - 1] != x)) ? 1 : 0;
+        }
+        scan[tid] = cnt;
+        __syncthreads();
+        for (int off = 1; off < kThreads; off <<= 1) {
+            const int add = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += add;
+            __syncthreads();
+        }
+        int w = scan[tid] - cnt;
+        for (int e = e0; e < min(e0 + per, P); ++e) {
+            const int x = sortbuf[e];
+            if (x != 0x7fffffff && (e == 0 || sortbuf[e - 1] != x)) list[w++] = x;
+        }
+        if (tid == kThreads - 1) n_ids_s = scan[tid];
+        __syncthreads();
+        const int n_ids = n_ids_s;
+        if (p.dbg_sel && t_split == 0) {
+            int32_t* dst = p.dbg_sel + (static_cast<int64_t>(row0) * p.Hkv + g) * (1 + p.n_sel);
+            if (tid == 0) dst[0] = n_ids;
+            for (int e = tid; e < n_ids; e += kThreads) dst[1 + e] = list[e];
+        }
+        n_slots = n_ids * p.bs;
+    }
+    __syncthreads();
+
+    // cell of key slot k (-1 when the slot holds no visible key for anybody)
+    auto slot_cell = [&](int k) -> int {
+        if (p.mode != kSel) return lo + k;
+        const int c = list[k / p.bs] * p.bs + k % p.bs;
+        return (c < p.n_kv && c >= lo && c < hi) ? c : -1;
+    };
+    // visibility of cell c for query vector i (c >= 0)
+    auto visible = [&](int i, int c) -> bool {
+        if (p.mode == kDecode) {
+            const int lim = p.causal ? min(qpos(i) + 1, kvl) : kvl;
+            return c < lim;
+        }
+        if (p.mode == kMask) {
+            const float mv = p.mask[static_cast<int64_t>(qrow(i)) * p.m_sr +
+                                    static_cast<int64_t>(qhead(i)) * p.m_sh + c];
+            if (mv == kNegInf) return false;
+            return !(p.causal && c > qpos(i));
+        }
+        return true;
+    };
+
+    const int NI = kThreads / D;                 // query-vector groups in the P.V step
+    const int d_own = tid % D;
+    const int ig = tid / D;
+    float acc[kQv];
+#pragma unroll
+    for (int u = 0; u < kQv; ++u) acc[u] = 0.f;
+
+    for (int t0 = 0; t0 < n_slots; t0 += kTile) {
+        if (tid < kTile) {
+            const int k = t0 + tid;
+            cell_t[tid] = k < n_slots ? slot_cell(k) : -1;
+        }
+        __syncthreads();
+        // visibility bits (also decides which keys are loaded at all)
+        if (tid < nq) {
+            uint32_t bits = 0;
+            for (int s = 0; s < kTile; ++s) {
+                const int c = cell_t[s];
+                if (c >= 0 && visible(tid, c)) bits |= 1u << s;
+            }
+            vis[tid] = bits;
+        }
+        __syncthreads();
+        uint32_t any = 0;
+        for (int i = 0; i < nq; ++i) any |= vis[i];
+        if (any == 0) {            // nobody sees this tile: nothing is read
+            __syncthreads();
+            continue;
+        }
+        // stage K and V of the keys somebody sees
+        for (int e = tid; e < kTile * D; e += kThreads) {
+            const int s = e / D, d = e % D;
+            const int c = cell_t[s];
+            float kx = 0.f, vx = 0.f;
+            if (c >= 0 && ((any >> s) & 1u)) {
+                const int64_t base = (p.mode == kDecode ? static_cast<int64_t>(b) * p.kv_ss : 0) +
+                                     static_cast<int64_t>(c) * p.kv_sc +
+                                     static_cast<int64_t>(g) * p.kv_sh;
+                kx = load_kv_elem(p.k, base + d, p.dt);
+                vx = load_kv_elem(p.v, base + d, p.dt);
+                if (p.dt == SEL_ATTN_I8) {
+                    const int64_t sb = (p.mode == kDecode ? static_cast<int64_t>(b) * p.sc_ss : 0) +
+                                       static_cast<int64_t>(c) * p.sc_sc +
+                                       static_cast<int64_t>(g) * p.sc_sh;
+                    kx *= p.ksc[sb];
+                    vx *= p.vsc[sb];
+                }
+            }
+            kt[s * (kMaxD + 1) + d] = kx;
+            vt[s * kMaxD + d] = vx;
+        }
+        __syncthreads();
+        // scores of visible pairs
+        for (int e = tid; e < kQv * kTile; e += kThreads) {
+            const int i = e / kTile, s = e % kTile;
+            if (i >= nq || !((vis[i] >> s) & 1u)) continue;
+            float dot = 0.f;
+            const float* qi = qs + i * kMaxD;
+            const float* ks = kt + s * (kMaxD + 1);
+            for (int d = 0; d < D; ++d) dot = fmaf(qi[d], ks[d], dot);
+            const int c = cell_t[s];
+            const float slope = p.alibi ? p.alibi[qhead(i)] : 0.f;
+            const float mv = p.mode == kMask
+                                 ? p.mask[static_cast<int64_t>(qrow(i)) * p.m_sr +
+                                          static_cast<int64_t>(qhead(i)) * p.m_sh + c]
+                                 : 0.f;
+            ps[i * kTile + s] = score_pipeline(dot, p.scale, p.softcap, slope, c - qpos(i), mv);
+        }
+        __syncthreads();
+        // online softmax update, one thread per query vector
+        if (tid < nq) {
+            const int i = tid;
+            const uint32_t bits = vis[i];
+            float mt = kNegInf;
+            int nanf = nan_run[i];
+            for (int s = 0; s < kTile; ++s) {
+                if (!((bits >> s) & 1u)) continue;
+                const float x = ps[i * kTile + s];
+                if (x != x) nanf = 1;
+                else mt = max_keep(mt, x);
+            }
+            const float m_old = m_run[i];
+            const float m_new = max_keep(m_old, mt);
+            const float c = rescale_factor(m_old, m_new);
+            float lsum = 0.f;
+            const bool first_head = ((p.mode == kDecode ? m0 + i : i) % G) == 0;
+            for (int s = 0; s < kTile; ++s) {
+                if (!((bits >> s) & 1u)) continue;
+                const float x = ps[i * kTile + s];
+                const float pe = exp_diff(x, m_new);
+                ps[i * kTile + s] = pe;
+                lsum += pe;
+                if (first_head) {
+                    const long long cc = cell_t[s];
+                    dbg[i][0] += 1;
+                    dbg[i][1] += cc;
+                    dbg[i][2] += cc * cc;
+                }
+            }
+            l_run[i] = l_run[i] * c + lsum;
+            m_run[i] = m_new;
+            c_run[i] = c;
+            nan_run[i] = nanf;
+        }
+        __syncthreads();
+        // o = o * c + sum_s p_s v_s over visible keys only
+        if (ig < NI) {
+            for (int u = 0; u < kQv; ++u) {
+                const int i = ig + u * NI;
+                if (i >= nq) break;
+                const uint32_t bits = vis[i];
+                float a = acc[u] * c_run[i];
+                for (int s = 0; s < kTile; ++s) {
+                    if ((bits >> s) & 1u) a = fmaf(ps[i * kTile + s], vt[s * kMaxD + d_own], a);
+                }
+                acc[u] = a;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue -----------------------------------------------------------
+    if (ig < NI) {
+        for (int u = 0; u < kQv; ++u) {
+            const int i = ig + u * NI;
+            if (i >= nq) break;
+            const int r = qrow(i), h = qhead(i);
+            const float m = m_run[i], l = l_run[i];
+            const bool bad = nan_run[i] || m == kPosInf;
+            const bool empty = !bad && m == kNegInf;
+            const bool split = p.mode == kDecode || p.n_splits > 1;
+            if (!split) {
+                float o = bad ? __builtin_nanf("") : (empty ? 0.f : acc[u] / l);
+                p.out[(static_cast<int64_t>(r) * p.Hq + h) * D + d_own] = o;
+            } else {
+                int64_t pi;
+                if (p.mode == kDecode)
+                    pi = ((static_cast<int64_t>(b) * p.R + r) * p.Hq + h) * p.n_slices_max + t_split;
+                else
+                    pi = (static_cast<int64_t>(r) * p.Hq + h) * p.n_splits + t_split;
+                p.part_o[pi * D + d_own] = empty ? 0.f : acc[u];
+                if (d_own == 0) {
+                    p.part_ml[pi * 2 + 0] = nan_run[i] ? __builtin_nanf("") : m;
+                    p.part_ml[pi * 2 + 1] = bad ? __builtin_nanf("") : (empty ? 0.f : l);
+                }
+            }
+        }
+    }
+    if (p.dbg_visit && tid < nq) {
+        const int i = tid;
+        const bool first_head = ((p.mode == kDecode ? m0 + i : i) % G) == 0;
+        if (first_head) {
+            const int r = qrow(i);
+            int64_t di;
+            if (p.mode == kDecode)
+                di = ((static_cast<int64_t>(b) * p.R + r) * p.Hkv + g) * p.n_slices_max + t_split;
+            else
+                di = (static_cast<int64_t>(r) * p.Hkv + g) * p.n_splits + t_split;
+            p.dbg_visit[di * 3 + 0] = dbg[i][0];
+            p.dbg_visit[di * 3 + 1] = dbg[i][1];
+            p.dbg_visit[di * 3 + 2] = dbg[i][2];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// split combine
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void combine_kernel(sel_attn_combine_args a) {
+    const int64_t unit = blockIdx.x;              // (b, r, h)
+    const int D = a.head_dim;
+    const int b = static_cast<int>(unit / (static_cast<int64_t>(a.n_row) * a.n_head_q));
+    int ns = a.n_slices_max;
+    if (a.kv_len) {
+        const int n = min(max(a.kv_len[b], 0), a.cap);
+        ns = min((n + a.slice_len - 1) / a.slice_len, a.n_slices_max);
+    }
+    const float* ml = a.part_ml + unit * a.n_slices_max * 2;
+    const float* po = a.part_o + unit * a.n_slices_max * D;
+    float* out = a.out + unit * D;
+    bool nanf = false;
+    float M = kNegInf;
+    for (int t = 0; t < ns; ++t) {
+        const float m = ml[2 * t];
+        if (m != m) nanf = true;
+        else M = max_keep(M, m);
+    }
+    const int per = D / 64;                       // 1, 2 or 4 dims per lane
+    const int d0 = threadIdx.x * per;
+    if (nanf || M == kPosInf) {
+        for (int e = 0; e < per; ++e) out[d0 + e] = __builtin_nanf("");
+        return;
+    }
+    if (M == kNegInf) {
+        for (int e = 0; e < per; ++e) out[d0 + e] = 0.f;
+        return;
+    }
+    float num[4] = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    for (int t = 0; t < ns; ++t) {
+        const float m = ml[2 * t];
+        if (m == kNegInf) continue;
+        const float w = exp2f((m - M) * kLog2e);
+        den = fmaf(w, ml[2 * t + 1], den);
+        for (int e = 0; e < per; ++e) num[e] = fmaf(w, po[static_cast<int64_t>(t) * D + d0 + e], num[e]);
+    }
+    for (int e = 0; e < per; ++e) out[d0 + e] = num[e] / den;
+}
+
+int next_pow2(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+hipError_t prepare_kernel() {
+    static bool done = false;
+    if (!done) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&valu_attn_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+        if (e != hipSuccess) return e;
+        done = true;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_valu_decode(const sel_attn_decode_args& a, hipStream_t st) {
+    hipError_t e = prepare_kernel();
+    if (e != hipSuccess) return e;
+    ValuParams p{};
+    p.mode = kDecode;
+    p.Hq = a.n_head_q; p.Hkv = a.n_head_kv; p.G = a.n_head_q / a.n_head_kv; p.D = a.head_dim;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.dt = a.kv_dtype;
+    p.kv_ss = a.kv_stride_stream; p.kv_sc = a.kv_stride_cell; p.kv_sh = a.kv_stride_head;
+    p.ksc = a.k_scale; p.vsc = a.v_scale;
+    p.sc_ss = a.sc_stride_stream; p.sc_sc = a.sc_stride_cell; p.sc_sh = a.sc_stride_head;
+    p.scale = a.scale; p.softcap = a.softcap; p.alibi = a.alibi_slopes;
+    p.S = a.n_stream; p.R = a.n_row; p.cap = a.cap; p.kv_len = a.kv_len; p.causal = a.causal;
+    p.slice_len = a.slice_len; p.n_slices_max = a.n_slices_max;
+    p.n_qchunks = (a.n_row * p.G + kQv - 1) / kQv;
+    p.part_o = a.part_o; p.part_ml = a.part_ml; p.dbg_visit = a.dbg_visit;
+    const int n_sl = std::min(a.n_slices_max, (a.cap + a.slice_len - 1) / a.slice_len);
+    dim3 grid(n_sl, a.n_head_kv * p.n_qchunks, a.n_stream);
+    hipLaunchKernelGGL(valu_attn_kernel, grid, dim3(kThreads), kSmemBytes, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_valu_prefill(const sel_attn_prefill_args& a, hipStream_t st) {
+    hipError_t e = prepare_kernel();
+    if (e != hipSuccess) return e;
+    ValuParams p{};
+    p.mode = a.sel ? kSel : kMask;
+    p.Hq = a.n_head_q; p.Hkv = a.n_head_kv; p.G = a.n_head_q / a.n_head_kv; p.D = a.head_dim;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.dt = a.kv_dtype;
+    p.kv_sc = a.kv_stride_cell; p.kv_sh = a.kv_stride_head;
+    p.ksc = a.k_scale; p.vsc = a.v_scale;
+    p.sc_sc = a.sc_stride_cell; p.sc_sh = a.sc_stride_head;
+    p.scale = a.scale; p.softcap = a.softcap; p.alibi = a.alibi_slopes;
+    p.R = a.n_row; p.n_kv = a.n_kv; p.q_pos = a.q_pos;
+    p.sel = a.sel; p.n_sel = a.n_sel; p.bs = a.block_size; p.sel_pow2 = a.sel ? next_pow2(a.n_sel) : 0;
+    p.mask = a.mask; p.m_sr = a.mask_stride_row; p.m_sh = a.mask_stride_head; p.causal = a.causal;
+    p.n_splits = a.n_splits;
+    p.split_step = (a.n_kv + a.n_splits - 1) / a.n_splits;
+    p.rows_per_wg = a.sel ? 1 : std::max(1, kQv / p.G);
+    p.out = a.out; p.part_o = a.part_o; p.part_ml = a.part_ml;
+    p.dbg_visit = a.dbg_visit; p.dbg_sel = a.dbg_sel;
+    const int n_rb = (a.n_row + p.rows_per_wg - 1) / p.rows_per_wg;
+    dim3 grid(a.n_splits, a.n_head_kv, n_rb);
+    hipLaunchKernelGGL(valu_attn_kernel, grid, dim3(kThreads), kSmemBytes, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const sel_attn_combine_args& a, hipStream_t st) {
+    const int64_t units = static_cast<int64_t>(a.n_stream) * a.n_row * a.n_head_q;
+    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(units)), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace selattn

@@ -1,0 +1,52 @@
+"""The 16x16x32 MFMA lane layout that the matrix-core kernels rely on, checked
+on the GPU with exact small-integer inputs (one wave, fixed 64-lane buffers)."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "probe", "libmfma_probe.so")
+
+
+def expected(a_vals, b_vals):
+    # A[m][k] held by lane (k // 8) * 16 + m, element k % 8; B[k][n] by lane (k // 8) * 16 + n
+    A = np.zeros((16, 32))
+    B = np.zeros((32, 16))
+    for l in range(64):
+        for j in range(8):
+            A[l % 16, 8 * (l // 16) + j] = a_vals[l, j]
+            B[8 * (l // 16) + j, l % 16] = b_vals[l, j]
+    C = A @ B
+    d = np.zeros((64, 4))
+    for l in range(64):
+        for i in range(4):
+            d[l, i] = C[4 * (l // 16) + i, l % 16]
+    return d
+
+
+@pytest.mark.parametrize("f16", [0, 1])
+def test_mfma_16x16x32_layout(f16):
+    if not torch.cuda.is_available():
+        pytest.fail("needs a GPU")
+    lib = ctypes.CDLL(LIB)
+    rng = np.random.default_rng(3)
+    a_vals = rng.integers(-4, 5, size=(64, 8)).astype(np.float32)
+    b_vals = rng.integers(-4, 5, size=(64, 8)).astype(np.float32)
+    if f16:
+        a_bits = a_vals.astype(np.float16).view(np.uint16)
+        b_bits = b_vals.astype(np.float16).view(np.uint16)
+    else:
+        a_bits = (a_vals.view(np.uint32) >> 16).astype(np.uint16)
+        b_bits = (b_vals.view(np.uint32) >> 16).astype(np.uint16)
+    a = torch.from_numpy(a_bits.view(np.int16).copy()).cuda()
+    b = torch.from_numpy(b_bits.view(np.int16).copy()).cuda()
+    d = torch.zeros((64, 4), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert lib.mfma_probe(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                          ctypes.c_void_p(d.data_ptr()), f16, ctypes.c_void_p(st)) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy(), expected(a_vals, b_vals))

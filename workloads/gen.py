@@ -178,21 +178,51 @@ class PrefillWorkload:
 # generic builders (tests use them at small sizes)
 # ----------------------------------------------------------------------------
 
+def _draw_kv_prefix(rng, n_stream, cap, n_head_kv, head_dim, dtype, kv_len):
+    """K or V for cells [0, kv_len[b]) of each stream; unused capacity is NaN
+    (int8: 0 with a NaN row scale), so a read past kv_len cannot go unnoticed."""
+    shape = (n_stream, cap, n_head_kv, head_dim)
+    if dtype == "f32":
+        store = np.full(shape, np.nan, np.float32)
+    elif dtype == "f16":
+        store = np.full(shape, np.nan, np.float16)
+    elif dtype == "bf16":
+        store = np.full(shape, 0x7FC0, np.uint16)
+    else:
+        store = np.zeros(shape, np.int8)
+    scales = np.full((n_stream, cap, n_head_kv), np.nan, np.float32) if dtype == "i8" else None
+    for b in range(n_stream):
+        n = int(kv_len[b])
+        x = rng.standard_normal((n, n_head_kv, head_dim), dtype=np.float32)
+        st, sc = _to_storage(x, dtype)
+        store[b, :n] = st
+        if sc is not None:
+            scales[b, :n] = sc
+    return store, scales
+
+
 def make_decode(*, seed, n_stream, n_row, n_head_q, n_head_kv, head_dim, cap,
                 kv_dtype, depths=None, depth_range=None, causal=True,
                 slice_len=1024, scale=None, softcap=0.0, alibi=False,
                 name="decode") -> DecodeWorkload:
-    """Decode workload: Q, K, V ~ N(0,1), then kv_len (given or drawn)."""
+    """Decode workload.
+
+    With fixed `depths`: Q, K, V ~ N(0,1) over the whole capacity, in that order.
+    With `depth_range`: Q, then the depths U[lo, hi] (inclusive), then K and V
+    for the cells below each depth only (unused capacity holds NaN).
+    """
     assert kv_dtype in KV_DTYPES
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((n_stream, n_row, n_head_q, head_dim), dtype=np.float32)
-    k, ks = _draw_kv(rng, (n_stream, cap, n_head_kv), head_dim, kv_dtype)
-    v, vs = _draw_kv(rng, (n_stream, cap, n_head_kv), head_dim, kv_dtype)
     if depths is not None:
+        k, ks = _draw_kv(rng, (n_stream, cap, n_head_kv), head_dim, kv_dtype)
+        v, vs = _draw_kv(rng, (n_stream, cap, n_head_kv), head_dim, kv_dtype)
         kv_len = np.asarray(depths, dtype=np.int32).reshape(n_stream)
     else:
         lo, hi = depth_range
         kv_len = rng.integers(lo, hi, size=n_stream, endpoint=True).astype(np.int32)
+        k, ks = _draw_kv_prefix(rng, n_stream, cap, n_head_kv, head_dim, kv_dtype, kv_len)
+        v, vs = _draw_kv_prefix(rng, n_stream, cap, n_head_kv, head_dim, kv_dtype, kv_len)
     if scale is None:
         scale = 1.0 / np.sqrt(head_dim)
     slopes = alibi_slopes(n_head_q) if alibi else None
