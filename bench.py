@@ -41,6 +41,10 @@ def parse():
     return ap.parse_args()
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def timed(fn, steps, torch):
     """Average ms of `fn` over `steps` back-to-back calls, HIP events on the current stream."""
     s = torch.cuda.current_stream()
@@ -94,10 +98,12 @@ def main():
     sa.lib()
 
     # ---- inputs (host generation, then resident in HBM) --------------------------
+    log("generating the split-K decode workload")
     wl2 = gen.config2()
     d2 = hip_run.DecodeDev(wl2, "cuda", poison_outputs=False)
     a2 = d2.args()
     c2 = d2.combine_args()
+    log("generating the selected-key prefill workload")
     wl3 = gen.config3()
     d3 = hip_run.PrefillDev(wl3, "cuda", poison_outputs=False)
     a3 = d3.args()
@@ -118,6 +124,7 @@ def main():
     def copy():
         copy_dst.copy_(copy_src)
 
+    log("warmup")
     for _ in range(args.warmup):
         step()
         prefill()
@@ -125,6 +132,7 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps -------------------------------------------
+    log("timing")
     ms_step = timed(step, args.steps, torch)
     ms_decode = timed(decode_only, args.steps, torch)
     ms_prefill = timed(prefill, args.steps, torch)
@@ -177,6 +185,7 @@ def main():
     }
 
     if args.verify:
+        log("generating the int8 verify-window workload")
         wl5 = gen.config5(32000)
         d5 = hip_run.DecodeDev(wl5, "cuda", poison_outputs=False)
         a5, c5 = d5.args(), d5.combine_args()
@@ -198,6 +207,7 @@ def main():
         del d5
 
     if not args.no_cpu_baseline:
+        log("timing the FP64 oracle on a sample")
         result["cpu_baseline"] = cpu_baseline_decode(wl2, streams=2)
 
     print(json.dumps(result), flush=True)
