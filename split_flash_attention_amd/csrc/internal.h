@@ -19,5 +19,7 @@ bool mfma_decode_eligible(const sel_attn_decode_args& a);
 hipError_t launch_mfma_decode(const sel_attn_decode_args& a, hipStream_t st);
 bool mfma_prefill_eligible(const sel_attn_prefill_args& a);
 hipError_t launch_mfma_prefill(const sel_attn_prefill_args& a, hipStream_t st);
+hipError_t launch_mfma_prefill_sel(const sel_attn_prefill_args& a, hipStream_t st);
+hipError_t launch_mfma_prefill_mask(const sel_attn_prefill_args& a, hipStream_t st);
 
 }  // namespace selattn

@@ -1,0 +1,31 @@
+// Split-K decode and verify windows on the matrix-core kernel: one work-group
+// per (stream, kv head, slice[, query chunk]) (TensorFold PR #2595: the
+// attn_decode grid of rows, heads and slices), partials merged by the combine.
+#include "mfma_kernel.h"
+
+#include <algorithm>
+
+namespace selattn {
+
+hipError_t launch_mfma_decode(const sel_attn_decode_args& a, hipStream_t st) {
+    using namespace mk;
+    MParams p{};
+    p.Hq = a.n_head_q; p.Hkv = a.n_head_kv; p.G = a.n_head_q / a.n_head_kv; p.D = a.head_dim;
+    p.M = a.n_row * p.G;
+    const Shape sh = pick_shape(p.M);
+    p.qpw = sh.waves * sh.qb * 16;
+    p.q = a.q; p.k = a.k; p.v = a.v;
+    p.kv_ss = a.kv_stride_stream; p.kv_sc = a.kv_stride_cell; p.kv_sh = a.kv_stride_head;
+    p.ksc = a.k_scale; p.vsc = a.v_scale;
+    p.sc_ss = a.sc_stride_stream; p.sc_sc = a.sc_stride_cell; p.sc_sh = a.sc_stride_head;
+    p.scale = a.scale; p.softcap = a.softcap; p.alibi = a.alibi_slopes;
+    p.R = a.n_row; p.cap = a.cap; p.kv_len = a.kv_len; p.causal = a.causal;
+    p.slice_len = a.slice_len; p.n_slices_max = a.n_slices_max;
+    p.part_o = a.part_o; p.part_ml = a.part_ml; p.dbg_visit = a.dbg_visit;
+    const int nqc = (p.M + p.qpw - 1) / p.qpw;
+    const int n_sl = std::min(a.n_slices_max, (a.cap + a.slice_len - 1) / a.slice_len);
+    dim3 grid(n_sl, a.n_head_kv * nqc, a.n_stream);
+    return launch_mode<kDecode>(a.kv_dtype, p, grid, sh, st);
+}
+
+}  // namespace selattn

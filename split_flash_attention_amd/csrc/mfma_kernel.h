@@ -1,0 +1,643 @@
+// Matrix-core (MFMA) flash attention kernel template for gfx950: split-K decode
+// and verify windows, prefill in selection or mask mode, bf16 / fp16 / int8 K/V.
+//
+// A query vector is one (row, query head) pair of one kv head.  A wave owns QB
+// blocks of 16 query vectors; the W waves of a work-group share each 32-key
+// tile of K and V staged in LDS:
+//   * K tile  [32 keys][D] 16-bit, 16-byte chunks XOR-swizzled by key;
+//   * V tile  transposed [D][32], keys in the contraction order of P^T below.
+// Scores are computed transposed, S^T[key][qv] = K . Q^T (one MFMA per 16 keys
+// x 32 dims), so each lane ends up holding 8 scores of ONE query vector.  The
+// online softmax of TensorFold PR #985 ("What this changes": running max per
+// fixed key tile, correction exp(m_old - m_new), l and o rescaled) then needs
+// only two cross-lane max exchanges per tile, and the lane's own 8 weights ARE
+// its P^T operand for O^T[dim][qv] += V^T . P^T (no data movement).
+//
+// Tiles are loaded into registers one tile ahead (every 16-byte load of a tile
+// is issued at once) and written to LDS at the top of the next iteration, so
+// HBM latency overlaps the matrix-core work of the current tile.
+//
+// Key sources: a contiguous slice (decode, TensorFold PR #2595: one
+// work-group per (stream, kv head, slice), partials merged afterwards), a
+// contiguous range with an F32 mask (HartsyInference PR #910), or the sorted,
+// de-duplicated selection list gathered in 32-cell tiles (strix-llama.cpp
+// PR #115, Vulkan selected-key commit message: one work-group per query x kv
+// head, list sorted in shared memory, invalid and repeated ids skipped).
+// A key no query vector of the work-group can see is never loaded.
+#pragma once
+
+#include "arch.h"
+#include "common.h"
+#include "internal.h"
+
+namespace selattn {
+namespace mk {
+
+constexpr int kTK = 32;          // keys per tile
+constexpr int kMaxSelM = 4096;   // longest selection list
+
+enum Mode : int { kDecode = 0, kMask = 1, kSel = 2 };
+
+struct MParams {
+    int Hq, Hkv, G, D;
+    int M;               // query vectors per (unit, kv head): R*G (decode), G (sel), rows*G (mask)
+    int qpw;             // query vectors per work-group = W * QB * 16
+    const float* q;
+    const void* k;
+    const void* v;
+    int64_t kv_ss, kv_sc, kv_sh;
+    const float* ksc;
+    const float* vsc;
+    int64_t sc_ss, sc_sc, sc_sh;
+    float scale, softcap;
+    const float* alibi;
+    // decode
+    int R, cap;
+    const int32_t* kv_len;
+    int causal;
+    int slice_len, n_slices_max;
+    // prefill
+    int n_kv;
+    const int32_t* q_pos;
+    const int32_t* sel;
+    int n_sel, bs, sel_pow2;
+    const float* mask;
+    int64_t m_sr, m_sh;
+    int rows_per_wg, n_splits, split_step;
+    // outputs
+    float* out;
+    float* part_o;
+    float* part_ml;
+    int64_t* dbg_visit;
+    int32_t* dbg_sel;
+};
+
+// ---------------------------------------------------------------------------
+// 16-bit conversions and LDS addressing
+// ---------------------------------------------------------------------------
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    uint16_t a, b;
+    if constexpr (F16) {
+        a = __builtin_bit_cast(uint16_t, static_cast<_Float16>(lo));
+        b = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hi));
+    } else {
+        a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
+        b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
+    }
+    return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+}
+
+// bf16 bits of int8 byte `byte` of `word` (exact: |x| <= 128 fits 8 significant bits)
+__device__ __forceinline__ uint32_t i8_to_bf16(uint32_t word, int byte) {
+    const float f = static_cast<float>(static_cast<int8_t>((word >> (8 * byte)) & 0xffu));
+    return __float_as_uint(f) >> 16;
+}
+
+// byte offset of 16-byte chunk `ch` (8 dims) of key row `key` in the K tile
+__device__ __forceinline__ int k_off(int key, int ch, int D) {
+    return key * D * 2 + ((ch ^ (key & 7)) << 4);
+}
+// byte offset of contraction chunk `cc` (8 keys) of dim row `d` in the V^T tile
+__device__ __forceinline__ int vt_off(int d, int cc) {
+    return d * 64 + ((cc ^ ((d >> 1) & 3)) << 4);
+}
+
+template <int D, bool SEL>
+constexpr int smem_bytes() {
+    return kTK * D * 2 + D * 64 + 2 * kTK * 4 + (SEL ? kMaxSelM * 4 : 0);
+}
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+template <int MODE, int KT, int D, int QB, int W>
+__global__ __launch_bounds__(64 * W) void mfma_attn_kernel(MParams p) {
+    constexpr bool F16 = (KT == SEL_ATTN_F16);
+    constexpr bool I8 = (KT == SEL_ATTN_I8);
+    constexpr int NKK = D / 32;                  // contraction steps for S^T
+    constexpr int NDB = D / 16;                  // dim blocks of O^T
+    constexpr int GCH = I8 ? D / 16 : D / 8;     // 16-byte chunks per K/V row in memory
+    constexpr int NT = 64 * W;
+    constexpr int K_TASKS = kTK * GCH;           // one 16-byte load each
+    constexpr int V_TASKS = 8 * GCH;             // four 16-byte loads each (4 consecutive keys)
+    constexpr int NKL = (K_TASKS + NT - 1) / NT;
+    constexpr int NVL = (V_TASKS + NT - 1) / NT;
+    constexpr int EPC = I8 ? 16 : 8;             // elements per 16-byte chunk
+
+    extern __shared__ __align__(16) char smem[];
+    char* k_lds = smem;                                            // kTK * D * 2
+    char* vt_lds = smem + kTK * D * 2;                             // D * 64
+    float* ksc_lds = reinterpret_cast<float*>(vt_lds + D * 64);    // kTK
+    float* vsc_lds = ksc_lds + kTK;                                // kTK
+    int* list = reinterpret_cast<int*>(vsc_lds + kTK);             // kMaxSelM (selection)
+
+    __shared__ int s_nids;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int ln = lane & 15;        // query vector of a block / key row of a 16-key block
+    const int lg = lane >> 4;        // lane group 0..3
+    const int G = p.G;
+
+    // ---- work unit ---------------------------------------------------------
+    const int t_split = blockIdx.x;
+    const int g = blockIdx.y % p.Hkv;
+    const int qchunk = blockIdx.y / p.Hkv;
+    int b = 0, kvl = 0, lo = 0, hi = 0, row0 = 0;
+    if constexpr (MODE == kDecode) {
+        b = blockIdx.z;
+        kvl = min(max(p.kv_len[b], 0), p.cap);
+        lo = t_split * p.slice_len;
+        if (lo >= kvl) return;            // past this stream's slices: nothing written
+        hi = min(lo + p.slice_len, kvl);
+    } else {
+        row0 = blockIdx.z * p.rows_per_wg;
+        lo = t_split * p.split_step;
+        hi = min(lo + p.split_step, p.n_kv);
+    }
+    const int m_wg = qchunk * p.qpw;               // first query vector of the work-group
+    const int m_wave = m_wg + wave * QB * 16;       // first of this wave
+
+    // query vector -> (row, head, position, causal limit)
+    int qv_row[QB], qv_head[QB], qv_pos[QB], qv_lim[QB];
+    bool qv_ok[QB];
+#pragma unroll
+    for (int k = 0; k < QB; ++k) {
+        const int m = m_wave + 16 * k + ln;
+        bool ok = m < p.M && m < m_wg + p.qpw;
+        int r, h;
+        if constexpr (MODE == kDecode) { r = m / G; h = g * G + m % G; ok = ok && r < p.R; }
+        else if constexpr (MODE == kSel) { r = row0; h = g * G + m; }
+        else { r = row0 + m / G; h = g * G + m % G; ok = ok && r < min(row0 + p.rows_per_wg, p.R); }
+        if (!ok) {                        // padding: point at a real row, never used
+            r = (MODE == kDecode) ? 0 : row0;
+            h = g * G;
+        }
+        qv_ok[k] = ok;
+        qv_row[k] = r;
+        qv_head[k] = h;
+        if constexpr (MODE == kDecode) {
+            qv_pos[k] = kvl - p.R + r;
+            qv_lim[k] = p.causal ? min(qv_pos[k] + 1, kvl) : kvl;
+        } else {
+            qv_pos[k] = p.q_pos ? p.q_pos[r] : 0;
+            qv_lim[k] = (MODE == kMask && p.causal) ? qv_pos[k] + 1 : 0x7fffffff;
+        }
+        if (!ok) qv_lim[k] = -1;          // sees nothing
+    }
+
+    // ---- Q^T operands (scale folded in) ----------------------------------
+    u32x4 qop[QB][NKK];
+#pragma unroll
+    for (int k = 0; k < QB; ++k) {
+        const float* qp;
+        if constexpr (MODE == kDecode)
+            qp = p.q + ((static_cast<int64_t>(b) * p.R + qv_row[k]) * p.Hq + qv_head[k]) * D;
+        else
+            qp = p.q + (static_cast<int64_t>(qv_row[k]) * p.Hq + qv_head[k]) * D;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            float x[8];
+            if (qv_ok[k]) {
+                const float4 a = *reinterpret_cast<const float4*>(qp + kk * 32 + 8 * lg);
+                const float4 c = *reinterpret_cast<const float4*>(qp + kk * 32 + 8 * lg + 4);
+                x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+                x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qop[k][kk][j] = pack2<F16>(x[2 * j] * p.scale, x[2 * j + 1] * p.scale);
+        }
+    }
+    float slope[QB];
+#pragma unroll
+    for (int k = 0; k < QB; ++k) slope[k] = (p.alibi && qv_ok[k]) ? p.alibi[qv_head[k]] : 0.f;
+
+    // ---- key slots to walk -------------------------------------------------
+    int n_keys = 0;
+    if constexpr (MODE == kSel) {
+        // the row's list: invalid ids become +inf, bitonic sort, then drop repeats
+        const int P = p.sel_pow2;
+        const int32_t* srow = p.sel + static_cast<int64_t>(row0) * p.n_sel;
+        for (int e = tid; e < P; e += NT) {
+            int id = 0x7fffffff;
+            if (e < p.n_sel) {
+                const int x = srow[e];
+                if (x >= 0 && static_cast<int64_t>(x) * p.bs < p.n_kv) id = x;
+            }
+            list[e] = id;
+        }
+        __syncthreads();
+        for (int kq = 2; kq <= P; kq <<= 1) {
+            for (int j = kq >> 1; j > 0; j >>= 1) {
+                for (int e = tid; e < P; e += NT) {
+                    const int o = e ^ j;
+                    if (o > e) {
+                        const int x = list[e], y = list[o];
+                        if ((x > y) == ((e & kq) == 0)) { list[e] = y; list[o] = x; }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        // stable in-place compaction by one lane: keeps the first of each run
+        if (tid == 0) {
+            int w = 0;
+            int prev = -1;
+            for (int e = 0; e < P; ++e) {
+                const int x = list[e];
+                if (x == 0x7fffffff) break;
+                if (x != prev) list[w++] = x;
+                prev = x;
+            }
+            s_nids = w;
+        }
+        __syncthreads();
+        const int n_ids = s_nids;
+        if (p.dbg_sel && t_split == 0) {
+            int32_t* dst = p.dbg_sel + (static_cast<int64_t>(row0) * p.Hkv + g) * (1 + p.n_sel);
+            if (tid == 0) dst[0] = n_ids;
+            for (int e = tid; e < n_ids; e += NT) dst[1 + e] = list[e];
+        }
+        n_keys = n_ids * p.bs;
+    } else {
+        // no query vector of this work-group sees keys at or past the largest limit
+        int lim_max = -1;
+        const int m_end = min(p.M, m_wg + p.qpw);
+        if (m_end > m_wg) {
+            const int rbase = (MODE == kDecode) ? 0 : row0;
+            const int r_first = rbase + m_wg / G;
+            const int r_last = rbase + (m_end - 1) / G;
+            for (int r = r_first; r <= r_last && r < p.R; ++r) {
+                int l;
+                if constexpr (MODE == kDecode) l = p.causal ? min(kvl - p.R + r + 1, kvl) : kvl;
+                else l = p.causal ? (p.q_pos[r] + 1) : hi;
+                lim_max = max(lim_max, l);
+            }
+        }
+        n_keys = max(0, min(hi, lim_max) - lo);
+    }
+
+    // cell of key slot `kslot` (-1 for none)
+    auto slot_cell = [&](int kslot) -> int {
+        if (kslot >= n_keys) return -1;
+        if constexpr (MODE == kSel) {
+            const int c = list[kslot / p.bs] * p.bs + kslot % p.bs;
+            return (c < p.n_kv && c >= lo && c < hi) ? c : -1;
+        } else {
+            return lo + kslot;
+        }
+    };
+
+    const int64_t kv_base = (MODE == kDecode ? static_cast<int64_t>(b) * p.kv_ss : 0) +
+                            static_cast<int64_t>(g) * p.kv_sh;
+    const int64_t sc_base = (MODE == kDecode ? static_cast<int64_t>(b) * p.sc_ss : 0) +
+                            static_cast<int64_t>(g) * p.sc_sh;
+    const char* kbase = static_cast<const char*>(p.k) + kv_base * (I8 ? 1 : 2);
+    const char* vbase = static_cast<const char*>(p.v) + kv_base * (I8 ? 1 : 2);
+    const int64_t cell_bytes = p.kv_sc * (I8 ? 1 : 2);
+
+    // ---- tile loads into registers -----------------------------------------
+    u32x4 kreg[NKL];
+    u32x4 vreg[NVL][4];
+    float kscr = 0.f, vscr = 0.f;
+    auto load_tile = [&](int t0) {
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) {
+            const int e = tid + i * NT;
+            kreg[i] = u32x4{0u, 0u, 0u, 0u};
+            if (e < K_TASKS) {
+                const int cell = slot_cell(t0 + e / GCH);
+                if (cell >= 0)
+                    kreg[i] = *reinterpret_cast<const u32x4*>(kbase + cell * cell_bytes + (e % GCH) * 16);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int e = tid + i * NT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                vreg[i][j] = u32x4{0u, 0u, 0u, 0u};
+                if (e < V_TASKS) {
+                    const int cell = slot_cell(t0 + 4 * (e / GCH) + j);
+                    if (cell >= 0)
+                        vreg[i][j] = *reinterpret_cast<const u32x4*>(vbase + cell * cell_bytes + (e % GCH) * 16);
+                }
+            }
+        }
+        if constexpr (I8) {
+            if (tid < kTK) {
+                const int cell = slot_cell(t0 + tid);
+                kscr = cell >= 0 ? p.ksc[sc_base + cell * p.sc_sc] : 0.f;
+                vscr = cell >= 0 ? p.vsc[sc_base + cell * p.sc_sc] : 0.f;
+            }
+        }
+    };
+    // registers -> LDS (K swizzled row-major, V transposed in contraction order)
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) {
+            const int e = tid + i * NT;
+            if (e < K_TASKS) {
+                const int key = e / GCH, ch = e % GCH;
+                if constexpr (I8) {
+                    const u32x4 r = kreg[i];
+                    u32x4 w0, w1;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        w0[2 * j] = i8_to_bf16(r[j], 0) | (i8_to_bf16(r[j], 1) << 16);
+                        w0[2 * j + 1] = i8_to_bf16(r[j], 2) | (i8_to_bf16(r[j], 3) << 16);
+                        w1[2 * j] = i8_to_bf16(r[2 + j], 0) | (i8_to_bf16(r[2 + j], 1) << 16);
+                        w1[2 * j + 1] = i8_to_bf16(r[2 + j], 2) | (i8_to_bf16(r[2 + j], 3) << 16);
+                    }
+                    *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch, D)) = w0;
+                    *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch + 1, D)) = w1;
+                } else {
+                    *reinterpret_cast<u32x4*>(k_lds + k_off(key, ch, D)) = kreg[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int e = tid + i * NT;
+            if (e < V_TASKS) {
+                const int kg = e / GCH, ch = e % GCH;
+                const int kb = kg >> 2, gq = kg & 3;       // keys kb*16 + 4*gq + j
+#pragma unroll
+                for (int dd = 0; dd < EPC; ++dd) {
+                    uint32_t lo2, hi2;
+                    if constexpr (I8) {
+                        const int w = dd >> 2, by = dd & 3;
+                        lo2 = i8_to_bf16(vreg[i][0][w], by) | (i8_to_bf16(vreg[i][1][w], by) << 16);
+                        hi2 = i8_to_bf16(vreg[i][2][w], by) | (i8_to_bf16(vreg[i][3][w], by) << 16);
+                    } else {
+                        const int w = dd >> 1;
+                        if (dd & 1) {
+                            lo2 = (vreg[i][0][w] >> 16) | (vreg[i][1][w] & 0xffff0000u);
+                            hi2 = (vreg[i][2][w] >> 16) | (vreg[i][3][w] & 0xffff0000u);
+                        } else {
+                            lo2 = (vreg[i][0][w] & 0xffffu) | (vreg[i][1][w] << 16);
+                            hi2 = (vreg[i][2][w] & 0xffffu) | (vreg[i][3][w] << 16);
+                        }
+                    }
+                    *reinterpret_cast<uint2*>(vt_lds + vt_off(ch * EPC + dd, gq) + 8 * kb) = uint2{lo2, hi2};
+                }
+            }
+        }
+        if constexpr (I8) {
+            if (tid < kTK) {
+                ksc_lds[tid] = kscr;
+                vsc_lds[tid] = vscr;
+            }
+        }
+    };
+
+    // ---- running state ---------------------------------------------------------
+    float m_run[QB], l_run[QB];
+    bool nan_run[QB];
+    f32x4 o_acc[QB][NDB];
+    long long dbg_cnt[QB], dbg_sum[QB], dbg_sq[QB];
+#pragma unroll
+    for (int k = 0; k < QB; ++k) {
+        m_run[k] = kNegInf;
+        l_run[k] = 0.f;
+        nan_run[k] = false;
+        dbg_cnt[k] = dbg_sum[k] = dbg_sq[k] = 0;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o_acc[k][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    if (n_keys > 0) load_tile(0);
+    for (int t0 = 0; t0 < n_keys; t0 += kTK) {
+        store_tile();
+        __syncthreads();
+        if (t0 + kTK < n_keys) load_tile(t0 + kTK);     // in flight during this tile's math
+
+        // ---- S^T = K . Q^T ----
+        f32x4 s[QB][2];
+#pragma unroll
+        for (int k = 0; k < QB; ++k) s[k][0] = s[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(k_lds + k_off(kb * 16 + ln, kk * 4 + lg, D));
+#pragma unroll
+                for (int k = 0; k < QB; ++k) s[k][kb] = mfma16x16x32<F16>(a, qop[k][kk], s[k][kb]);
+            }
+        }
+
+        // ---- score pipeline, visibility, online softmax ----
+        int cell_of[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cell_of[e] = slot_cell(t0 + (e >> 2) * 16 + 4 * lg + (e & 3));
+
+        u32x4 pop[QB];
+#pragma unroll
+        for (int k = 0; k < QB; ++k) {
+            float sc[8];
+            bool vis[8];
+            float tmax = kNegInf;
+            bool tnan = false;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kb = e >> 2, i = e & 3;
+                const int cell = cell_of[e];
+                bool v = cell >= 0 && cell < qv_lim[k];
+                float maskv = 0.f;
+                if constexpr (MODE == kMask) {
+                    if (v) {
+                        maskv = p.mask[static_cast<int64_t>(qv_row[k]) * p.m_sr +
+                                       static_cast<int64_t>(qv_head[k]) * p.m_sh + cell];
+                        v = maskv != kNegInf;
+                    }
+                }
+                float x = s[k][kb][i];
+                if constexpr (I8) x *= ksc_lds[kb * 16 + 4 * lg + i];
+                if (p.softcap > 0.f) x = p.softcap * tanhf(x / p.softcap);
+                x += slope[k] * static_cast<float>(cell - qv_pos[k]);
+                x += maskv;
+                vis[e] = v;
+                sc[e] = x;
+                if (v) {
+                    if (x != x) tnan = true;
+                    else tmax = max_keep(tmax, x);
+                }
+            }
+            // combine over the four lane groups that hold this query vector
+            tmax = max_keep(tmax, wave_xor(tmax, 16));
+            tmax = max_keep(tmax, wave_xor(tmax, 32));
+            int tn = tnan ? 1 : 0;
+            tn |= wave_xor_i(tn, 16);
+            tn |= wave_xor_i(tn, 32);
+            nan_run[k] = nan_run[k] || tn;
+            const float m_new = max_keep(m_run[k], tmax);
+            const float c = rescale_factor(m_run[k], m_new);
+            float pe[8];
+            float lsum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pe[e] = vis[e] ? exp_diff(sc[e], m_new) : 0.f;
+                lsum += pe[e];
+            }
+            l_run[k] = l_run[k] * c + lsum;
+            m_run[k] = m_new;
+            if (wave_any(c != 1.f)) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) o_acc[k][db] *= c;
+            }
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float w = pe[e];
+                if constexpr (I8) w *= vsc_lds[(e >> 2) * 16 + 4 * lg + (e & 3)];
+                pv[e] = w;
+            }
+            pop[k] = u32x4{pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]),
+                           pack2<F16>(pv[4], pv[5]), pack2<F16>(pv[6], pv[7])};
+            if (p.dbg_visit) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (vis[e]) {
+                        dbg_cnt[k] += 1;
+                        dbg_sum[k] += cell_of[e];
+                        dbg_sq[k] += static_cast<long long>(cell_of[e]) * cell_of[e];
+                    }
+                }
+            }
+        }
+
+        // ---- O^T += V^T . P^T ----
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(vt_lds + vt_off(db * 16 + ln, lg));
+#pragma unroll
+            for (int k = 0; k < QB; ++k) o_acc[k][db] = mfma16x16x32<F16>(a, pop[k], o_acc[k][db]);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue ---------------------------------------------------------------
+#pragma unroll
+    for (int k = 0; k < QB; ++k) {
+        float l = l_run[k];
+        l += wave_xor(l, 16);
+        l += wave_xor(l, 32);
+        long long cnt = 0, sum = 0, sq = 0;
+        if (p.dbg_visit) {
+            // the four lane groups of a query vector saw disjoint keys: add their counts
+            auto xsum = [&](long long v) -> long long {
+                long long acc = v;
+                for (int msk = 16; msk <= 32; msk <<= 1) {
+                    const unsigned lo32 = static_cast<unsigned>(acc & 0xffffffffLL);
+                    const int hi32 = static_cast<int>(acc >> 32);
+                    const unsigned olo = static_cast<unsigned>(wave_xor_i(static_cast<int>(lo32), msk));
+                    const int ohi = wave_xor_i(hi32, msk);
+                    acc += static_cast<long long>(
+                        (static_cast<unsigned long long>(static_cast<unsigned>(ohi)) << 32) | olo);
+                }
+                return acc;
+            };
+            cnt = xsum(dbg_cnt[k]);
+            sum = xsum(dbg_sum[k]);
+            sq = xsum(dbg_sq[k]);
+        }
+        if (!qv_ok[k]) continue;
+        const int r = qv_row[k], h = qv_head[k];
+        const float m = m_run[k];
+        const bool bad = nan_run[k] || m == kPosInf;
+        const bool empty = !bad && m == kNegInf;
+        const bool split = (MODE == kDecode) || p.n_splits > 1;
+        int64_t pi;
+        if constexpr (MODE == kDecode)
+            pi = ((static_cast<int64_t>(b) * p.R + r) * p.Hq + h) * p.n_slices_max + t_split;
+        else
+            pi = (static_cast<int64_t>(r) * p.Hq + h) * p.n_splits + t_split;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int d0 = db * 16 + 4 * lg;
+            float4 o;
+            if (!split) {
+                const float inv = 1.f / l;
+                if (bad) o = float4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+                else if (empty) o = float4{0.f, 0.f, 0.f, 0.f};
+                else o = float4{o_acc[k][db][0] * inv, o_acc[k][db][1] * inv, o_acc[k][db][2] * inv,
+                                o_acc[k][db][3] * inv};
+                *reinterpret_cast<float4*>(p.out + (static_cast<int64_t>(r) * p.Hq + h) * D + d0) = o;
+            } else {
+                if (empty) o = float4{0.f, 0.f, 0.f, 0.f};
+                else o = float4{o_acc[k][db][0], o_acc[k][db][1], o_acc[k][db][2], o_acc[k][db][3]};
+                *reinterpret_cast<float4*>(p.part_o + pi * D + d0) = o;
+            }
+        }
+        if (split && lg == 0) {
+            p.part_ml[pi * 2 + 0] = nan_run[k] ? __builtin_nanf("") : m;
+            p.part_ml[pi * 2 + 1] = bad ? __builtin_nanf("") : (empty ? 0.f : l);
+        }
+        if (p.dbg_visit && lg == 0) {
+            const int m_idx = m_wave + 16 * k + ln;
+            if (m_idx % G == 0) {           // the first query head of the row records its visits
+                int64_t di;
+                if constexpr (MODE == kDecode)
+                    di = ((static_cast<int64_t>(b) * p.R + r) * p.Hkv + g) * p.n_slices_max + t_split;
+                else
+                    di = (static_cast<int64_t>(r) * p.Hkv + g) * p.n_splits + t_split;
+                p.dbg_visit[di * 3 + 0] = cnt;
+                p.dbg_visit[di * 3 + 1] = sum;
+                p.dbg_visit[di * 3 + 2] = sq;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launch helpers
+// ---------------------------------------------------------------------------
+struct Shape {
+    int qb;      // query blocks per wave: 1, 2 or 3
+    int waves;   // waves per work-group: 1 or 4
+};
+
+inline Shape pick_shape(int M) {
+    const int nqb = (M + 15) / 16;
+    if (nqb <= 1) return {1, 1};
+    if (nqb <= 4) return {1, 4};
+    if (nqb <= 8) return {2, 4};
+    return {3, 4};
+}
+
+template <int MODE, int KT, int D, int QB, int W>
+hipError_t launch_one(const MParams& p, dim3 grid, hipStream_t st) {
+    constexpr int smem = smem_bytes<D, MODE == kSel>();
+    hipLaunchKernelGGL((mfma_attn_kernel<MODE, KT, D, QB, W>), grid, dim3(64 * W), smem, st, p);
+    return hipGetLastError();
+}
+
+template <int MODE, int KT, int D>
+hipError_t launch_shape(const MParams& p, dim3 grid, Shape sh, hipStream_t st) {
+    if (sh.waves == 1) return launch_one<MODE, KT, D, 1, 1>(p, grid, st);
+    switch (sh.qb) {
+    case 1: return launch_one<MODE, KT, D, 1, 4>(p, grid, st);
+    case 2: return launch_one<MODE, KT, D, 2, 4>(p, grid, st);
+    default: return launch_one<MODE, KT, D, 3, 4>(p, grid, st);
+    }
+}
+
+template <int MODE>
+hipError_t launch_mode(int dt, const MParams& p, dim3 grid, Shape sh, hipStream_t st) {
+    if (dt == SEL_ATTN_BF16)
+        return p.D == 256 ? launch_shape<MODE, SEL_ATTN_BF16, 256>(p, grid, sh, st)
+                          : launch_shape<MODE, SEL_ATTN_BF16, 128>(p, grid, sh, st);
+    if (dt == SEL_ATTN_F16)
+        return p.D == 256 ? launch_shape<MODE, SEL_ATTN_F16, 256>(p, grid, sh, st)
+                          : launch_shape<MODE, SEL_ATTN_F16, 128>(p, grid, sh, st);
+    return p.D == 256 ? launch_shape<MODE, SEL_ATTN_I8, 256>(p, grid, sh, st)
+                      : launch_shape<MODE, SEL_ATTN_I8, 128>(p, grid, sh, st);
+}
+
+}  // namespace mk
+}  // namespace selattn
