@@ -28,6 +28,23 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     }
 }
 
+// v_mfma_f32_16x16x16_{bf16,f16}: the same layout with 4 packed 16-bit values per
+// lane: A[l % 16][4 * (l / 16) + j], B[4 * (l / 16) + j][l % 16], j = 0..3.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+    if constexpr (F16) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                     __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                         __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+    }
+}
+
 // Butterfly exchange within the wave.
 __device__ __forceinline__ float wave_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
 __device__ __forceinline__ int wave_xor_i(int x, int mask) { return __shfl_xor(x, mask, 64); }

@@ -1,0 +1,530 @@
+// Single-wave matrix-core kernel for units of at most 16 query vectors: split-K
+// decode with R * G <= 16 (the whole GQA group of one row) and selection-mode
+// prefill with G <= 16.  Same arithmetic as mfma_kernel.h, shaped for HBM
+// streaming at two waves per SIMD:
+//   * 16-key tiles (K 16 x D and V^T D x 16 in LDS, 8 KiB each at D = 256), so the
+//     next tile's loads fit in 64 registers per lane and a work-group needs 16 KiB
+//     of LDS (plus the selection list);
+//   * S^T = K . Q^T on v_mfma_f32_16x16x32 (one MFMA per 32 dims), each lane then
+//     holds 4 scores of ONE query vector, which are exactly its P^T operand for
+//     O^T += V^T . P^T on v_mfma_f32_16x16x16;
+//   * lazy rescaling: the exponent reference m_use only moves when a score exceeds
+//     it by more than 8 (weights stay below e^8), so o and l are rarely rescaled;
+//     the true maximum is tracked alongside and applied once at the end, so the
+//     result is the same softmax (TensorFold PR #985, "What this changes": the
+//     correction exp(m_old - m_new) applied to l and o).
+#pragma once
+
+#include "mfma_kernel.h"
+
+namespace selattn {
+namespace mk {
+
+constexpr int kLT = 16;          // keys per tile
+constexpr float kLazy = 8.0f;    // slack of the exponent reference, natural units
+
+// K tile: 16 rows of D 16-bit values; 16-byte chunks XOR-ed with (key & 15), so the
+// 16 rows of one operand read land on 16 distinct chunks.
+__device__ __forceinline__ int k16_off(int key, int ch, int D) {
+    return key * D * 2 + ((ch ^ (key & 15)) << 4);
+}
+// V^T tile: row d holds 16 keys (32 bytes, four 8-byte slots of 4 keys).  Row d is
+// stored at pr = d ^ ((d >> 3) & 7) and slot s at s ^ (2 * ((pr >> 3) & 1)): both the
+// 16-row operand reads and the 32-lane staging writes then hit distinct banks.
+__device__ __forceinline__ int vt16_off(int d, int slot) {
+    const int pr = d ^ ((d >> 3) & 7);
+    return pr * 32 + ((slot ^ (((pr >> 3) & 1) << 1)) << 3);
+}
+
+template <int D>
+constexpr int lean_base_smem() {
+    return kLT * D * 2 + D * 32 + 2 * kLT * 4;
+}
+
+template <int MODE, int KT, int D>
+__device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, const int gy, const int bz,
+                                          char* smem, int& s_nids) {
+    constexpr bool F16 = (KT == SEL_ATTN_F16);
+    constexpr bool I8 = (KT == SEL_ATTN_I8);
+    constexpr int NKK = D / 32;
+    constexpr int NDB = D / 16;
+    constexpr int GCH = I8 ? D / 16 : D / 8;        // 16-byte chunks per K/V row in memory
+    constexpr int K_TASKS = kLT * GCH;              // one 16-byte load each
+    constexpr int V_TASKS = 4 * GCH;                // task e: keys 4*(e & 3) + 0..3, chunk e >> 2
+    constexpr int NKL = (K_TASKS + 63) / 64;
+    constexpr int NVL = (V_TASKS + 63) / 64;
+    constexpr int EPC = I8 ? 16 : 8;
+
+    char* k_lds = smem;
+    char* vt_lds = smem + kLT * D * 2;
+    float* ksc_lds = reinterpret_cast<float*>(vt_lds + D * 32);
+    float* vsc_lds = ksc_lds + kLT;
+    int* list = reinterpret_cast<int*>(vsc_lds + kLT);
+
+    const int lane = threadIdx.x;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    const int G = p.G;
+
+    // ---- work unit ---------------------------------------------------------
+    const int g = gy % p.Hkv;
+    const int qchunk = gy / p.Hkv;
+    int b = 0, kvl = 0, lo = 0, hi = 0, row0 = 0;
+    if constexpr (MODE == kDecode) {
+        b = bz;
+        kvl = min(max(p.kv_len[b], 0), p.cap);
+        lo = t_split * p.slice_len;
+        if (lo >= kvl) return;
+        hi = min(lo + p.slice_len, kvl);
+    } else {
+        row0 = bz;
+        lo = t_split * p.split_step;
+        hi = min(lo + p.split_step, p.n_kv);
+    }
+    const int m_wg = qchunk * 16;
+
+    // this lane's query vector
+    const int m = m_wg + ln;
+    bool ok = m < p.M;
+    int r, h;
+    if constexpr (MODE == kDecode) { r = m / G; h = g * G + m % G; ok = ok && r < p.R; }
+    else { r = row0; h = g * G + m; }
+    if (!ok) { r = (MODE == kDecode) ? 0 : row0; h = g * G; }
+    int pos, lim;
+    if constexpr (MODE == kDecode) {
+        pos = kvl - p.R + r;
+        lim = p.causal ? min(pos + 1, kvl) : kvl;
+    } else {
+        pos = p.q_pos ? p.q_pos[r] : 0;
+        lim = 0x7fffffff;
+    }
+    if (!ok) lim = -1;
+
+    // Q^T operands, scale folded in
+    u32x4 qop[NKK];
+    {
+        const float* qp = (MODE == kDecode)
+                              ? p.q + ((static_cast<int64_t>(b) * p.R + r) * p.Hq + h) * D
+                              : p.q + (static_cast<int64_t>(r) * p.Hq + h) * D;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            float x[8];
+            if (ok) {
+                const float4 a = *reinterpret_cast<const float4*>(qp + kk * 32 + 8 * lg);
+                const float4 c = *reinterpret_cast<const float4*>(qp + kk * 32 + 8 * lg + 4);
+                x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+                x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qop[kk][j] = pack2<F16>(x[2 * j] * p.scale, x[2 * j + 1] * p.scale);
+        }
+    }
+    const float slope = (p.alibi && ok) ? p.alibi[h] : 0.f;
+
+    // ---- key slots --------------------------------------------------------------
+    int n_keys;
+    if constexpr (MODE == kSel) {
+        const int P = p.sel_pow2;
+        const int32_t* srow = p.sel + static_cast<int64_t>(row0) * p.n_sel;
+        for (int e = lane; e < P; e += 64) {
+            int id = 0x7fffffff;
+            if (e < p.n_sel) {
+                const int x = srow[e];
+                if (x >= 0 && static_cast<int64_t>(x) * p.bs < p.n_kv) id = x;
+            }
+            list[e] = id;
+        }
+        __syncthreads();
+        for (int kq = 2; kq <= P; kq <<= 1) {
+            for (int j = kq >> 1; j > 0; j >>= 1) {
+                for (int e = lane; e < P; e += 64) {
+                    const int o = e ^ j;
+                    if (o > e) {
+                        const int x = list[e], y = list[o];
+                        if ((x > y) == ((e & kq) == 0)) { list[e] = y; list[o] = x; }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        if (lane == 0) {
+            int w = 0, prev = -1;
+            for (int e = 0; e < P; ++e) {
+                const int x = list[e];
+                if (x == 0x7fffffff) break;
+                if (x != prev) list[w++] = x;
+                prev = x;
+            }
+            s_nids = w;
+        }
+        __syncthreads();
+        const int n_ids = s_nids;
+        if (p.dbg_sel && t_split == 0 && qchunk == 0) {
+            int32_t* dst = p.dbg_sel + (static_cast<int64_t>(row0) * p.Hkv + g) * (1 + p.n_sel);
+            if (lane == 0) dst[0] = n_ids;
+            for (int e = lane; e < n_ids; e += 64) dst[1 + e] = list[e];
+        }
+        n_keys = n_ids * p.bs;
+    } else {
+        int lim_max = -1;
+        const int m_end = min(p.M, m_wg + 16);
+        for (int rr = m_wg / G; rr <= (m_end - 1) / G && rr < p.R; ++rr)
+            lim_max = max(lim_max, p.causal ? min(kvl - p.R + rr + 1, kvl) : kvl);
+        n_keys = max(0, min(hi, lim_max) - lo);
+    }
+
+    auto slot_cell = [&](int kslot) -> int {
+        if (kslot >= n_keys) return -1;
+        if constexpr (MODE == kSel) {
+            const int c = list[kslot / p.bs] * p.bs + kslot % p.bs;
+            return (c < p.n_kv && c >= lo && c < hi) ? c : -1;
+        } else {
+            return lo + kslot;
+        }
+    };
+
+    const int64_t kv_base = (MODE == kDecode ? static_cast<int64_t>(b) * p.kv_ss : 0) +
+                            static_cast<int64_t>(g) * p.kv_sh;
+    const int64_t sc_base = (MODE == kDecode ? static_cast<int64_t>(b) * p.sc_ss : 0) +
+                            static_cast<int64_t>(g) * p.sc_sh;
+    // K and V rows are read with buffer loads.  The descriptor of a decode unit
+    // starts at its first key row and ends at the end of its last visible row, so
+    // the rows past it (the tail of the last tile) read as zeros without a test;
+    // in selection mode it covers the whole cache and an absent cell gets an offset
+    // past the end.  Offsets are 32-bit (cell stride * cells < 2^31, checked on the host).
+    constexpr int ROWB = D * (I8 ? 1 : 2);
+    const int cb = static_cast<int>(p.kv_sc * (I8 ? 1 : 2));
+    const char* kbase = static_cast<const char*>(p.k) + kv_base * (I8 ? 1 : 2);
+    const char* vbase = static_cast<const char*>(p.v) + kv_base * (I8 ? 1 : 2);
+    int nrec;
+    if constexpr (MODE == kSel) {
+        nrec = (p.n_kv - 1) * cb + ROWB;
+    } else {
+        kbase += static_cast<int64_t>(lo) * cb;
+        vbase += static_cast<int64_t>(lo) * cb;
+        nrec = n_keys > 0 ? (n_keys - 1) * cb + ROWB : 0;
+    }
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), static_cast<short>(0), nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), static_cast<short>(0), nrec, 0x00020000);
+    constexpr int kAbsent = 0x7ffffff0;        // an offset past any descriptor's end
+    const int voff_k = (lane / GCH) * cb + (lane % GCH) * 16;            // decode: K task of lane
+    const int voff_v = 4 * (lane & 3) * cb + (lane >> 2) * 16;           // decode: V task of lane
+
+    u32x4 kreg[NKL];
+    u32x4 vreg[NVL][4];
+    float kscr = 0.f, vscr = 0.f;
+    auto load_tile = [&](int t0) {
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) {
+            const int e = lane + 64 * i;
+            if constexpr (MODE == kSel) {
+                const int cell = e < K_TASKS ? slot_cell(t0 + e / GCH) : -1;
+                const int off = cell >= 0 ? cell * cb + (e % GCH) * 16 : kAbsent;
+                kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+            } else {
+                const int off = e < K_TASKS ? voff_k : kAbsent;
+                kreg[i] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, t0 * cb + i * (64 / GCH) * cb, 0));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int e = lane + 64 * i;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (MODE == kSel) {
+                    const int cell = e < V_TASKS ? slot_cell(t0 + 4 * (e & 3) + j) : -1;
+                    const int off = cell >= 0 ? cell * cb + (e >> 2) * 16 : kAbsent;
+                    vreg[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+                } else {
+                    const int off = e < V_TASKS ? voff_v : kAbsent;
+                    vreg[i][j] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, (t0 + j) * cb + 256 * i, 0));
+                }
+            }
+        }
+        if constexpr (I8) {
+            if (lane < kLT) {
+                const int cell = slot_cell(t0 + lane);
+                kscr = cell >= 0 ? p.ksc[sc_base + cell * p.sc_sc] : 0.f;
+                vscr = cell >= 0 ? p.vsc[sc_base + cell * p.sc_sc] : 0.f;
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) {
+            const int e = lane + 64 * i;
+            if (e < K_TASKS) {
+                const int key = e / GCH, ch = e % GCH;
+                if constexpr (I8) {
+                    const u32x4 rw = kreg[i];
+                    u32x4 w0, w1;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        w0[2 * j] = i8_to_bf16(rw[j], 0) | (i8_to_bf16(rw[j], 1) << 16);
+                        w0[2 * j + 1] = i8_to_bf16(rw[j], 2) | (i8_to_bf16(rw[j], 3) << 16);
+                        w1[2 * j] = i8_to_bf16(rw[2 + j], 0) | (i8_to_bf16(rw[2 + j], 1) << 16);
+                        w1[2 * j + 1] = i8_to_bf16(rw[2 + j], 2) | (i8_to_bf16(rw[2 + j], 3) << 16);
+                    }
+                    *reinterpret_cast<u32x4*>(k_lds + k16_off(key, 2 * ch, D)) = w0;
+                    *reinterpret_cast<u32x4*>(k_lds + k16_off(key, 2 * ch + 1, D)) = w1;
+                } else {
+                    *reinterpret_cast<u32x4*>(k_lds + k16_off(key, ch, D)) = kreg[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int e = lane + 64 * i;
+            if (e < V_TASKS) {
+                const int kg = e & 3, ch = e >> 2;
+#pragma unroll
+                for (int dd = 0; dd < EPC; ++dd) {
+                    uint32_t lo2, hi2;
+                    if constexpr (I8) {
+                        const int w = dd >> 2, by = dd & 3;
+                        lo2 = i8_to_bf16(vreg[i][0][w], by) | (i8_to_bf16(vreg[i][1][w], by) << 16);
+                        hi2 = i8_to_bf16(vreg[i][2][w], by) | (i8_to_bf16(vreg[i][3][w], by) << 16);
+                    } else {
+                        const int w = dd >> 1;
+                        if (dd & 1) {
+                            lo2 = (vreg[i][0][w] >> 16) | (vreg[i][1][w] & 0xffff0000u);
+                            hi2 = (vreg[i][2][w] >> 16) | (vreg[i][3][w] & 0xffff0000u);
+                        } else {
+                            lo2 = (vreg[i][0][w] & 0xffffu) | (vreg[i][1][w] << 16);
+                            hi2 = (vreg[i][2][w] & 0xffffu) | (vreg[i][3][w] << 16);
+                        }
+                    }
+                    *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd, kg)) = uint2{lo2, hi2};
+                }
+            }
+        }
+        if constexpr (I8) {
+            if (lane < kLT) {
+                ksc_lds[lane] = kscr;
+                vsc_lds[lane] = vscr;
+            }
+        }
+    };
+
+    // ---- running state ---------------------------------------------------------
+    float m_use = kNegInf;     // exponent reference of o and l
+    float m_true = kNegInf;    // largest finite-or-infinite visible score seen
+    float l_run = 0.f;
+    bool nan_run = false;
+    long long dbg_cnt = 0, dbg_sum = 0, dbg_sq = 0;
+    f32x4 o_acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (n_keys > 0) load_tile(0);
+    for (int t0 = 0; t0 < n_keys; t0 += kLT) {
+        store_tile();
+        __syncthreads();
+        if (t0 + kLT < n_keys) load_tile(t0 + kLT);
+
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(k_lds + k16_off(ln, kk * 4 + lg, D));
+            s = mfma16x16x32<F16>(a, qop[kk], s);
+        }
+
+        float sc[4];
+        bool vis[4];
+        int cell_of[4];
+        float tmax = kNegInf;
+        bool tnan = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cell = slot_cell(t0 + 4 * lg + i);
+            cell_of[i] = cell;
+            const bool v = cell >= 0 && cell < lim;
+            float x = s[i];
+            if constexpr (I8) x *= ksc_lds[4 * lg + i];
+            if (p.softcap > 0.f) x = p.softcap * tanhf(x / p.softcap);
+            x += slope * static_cast<float>(cell - pos);
+            vis[i] = v;
+            sc[i] = x;
+            if (v) {
+                if (x != x) tnan = true;
+                else tmax = max_keep(tmax, x);
+            }
+        }
+        tmax = max_keep(tmax, wave_xor(tmax, 16));
+        tmax = max_keep(tmax, wave_xor(tmax, 32));
+        int tn = tnan ? 1 : 0;
+        tn |= wave_xor_i(tn, 16);
+        tn |= wave_xor_i(tn, 32);
+        nan_run = nan_run || tn;
+        m_true = max_keep(m_true, tmax);
+        const bool need = (tmax > m_use + kLazy) || (m_use == kNegInf && tmax != kNegInf);
+        if (wave_any(need)) {
+            const float c = need ? rescale_factor(m_use, tmax) : 1.f;
+            if (need) m_use = tmax;
+            l_run *= c;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o_acc[db] *= c;
+        }
+        float pe[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pe[i] = vis[i] ? exp_diff(sc[i], m_use) : 0.f;
+            l_run += pe[i];
+            if constexpr (I8) pe[i] *= vsc_lds[4 * lg + i];
+        }
+        const u32x2 pop = u32x2{pack2<F16>(pe[0], pe[1]), pack2<F16>(pe[2], pe[3])};
+        if (p.dbg_visit) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (vis[i]) {
+                    dbg_cnt += 1;
+                    dbg_sum += cell_of[i];
+                    dbg_sq += static_cast<long long>(cell_of[i]) * cell_of[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const u32x2 a = *reinterpret_cast<const u32x2*>(vt_lds + vt16_off(db * 16 + ln, lg));
+            o_acc[db] = mfma16x16x16<F16>(a, pop, o_acc[db]);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue ---------------------------------------------------------------
+    float l = l_run;
+    l += wave_xor(l, 16);
+    l += wave_xor(l, 32);
+    long long cnt = 0, sum = 0, sq = 0;
+    if (p.dbg_visit) {
+        auto xsum = [&](long long v) -> long long {
+            long long acc = v;
+            for (int msk = 16; msk <= 32; msk <<= 1) {
+                const unsigned lo32 = static_cast<unsigned>(acc & 0xffffffffLL);
+                const int hi32 = static_cast<int>(acc >> 32);
+                const unsigned olo = static_cast<unsigned>(wave_xor_i(static_cast<int>(lo32), msk));
+                const int ohi = wave_xor_i(hi32, msk);
+                acc += static_cast<long long>(
+                    (static_cast<unsigned long long>(static_cast<unsigned>(ohi)) << 32) | olo);
+            }
+            return acc;
+        };
+        cnt = xsum(dbg_cnt);
+        sum = xsum(dbg_sum);
+        sq = xsum(dbg_sq);
+    }
+    if (!ok) return;
+    const bool bad = nan_run || m_true == kPosInf;
+    const bool empty = !bad && m_true == kNegInf;
+    // move o and l from the lazy reference to the true maximum
+    float f = 1.f;
+    if (!bad && !empty && m_use != m_true) f = exp2f((m_use - m_true) * kLog2e);
+    l *= f;
+    const bool split = (MODE == kDecode) || p.n_splits > 1;
+    int64_t pi;
+    if constexpr (MODE == kDecode)
+        pi = ((static_cast<int64_t>(b) * p.R + r) * p.Hq + h) * p.n_slices_max + t_split;
+    else
+        pi = (static_cast<int64_t>(r) * p.Hq + h) * p.n_splits + t_split;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int d0 = db * 16 + 4 * lg;
+        float4 o;
+        if (!split) {
+            const float inv = f / l;
+            if (bad) o = float4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+            else if (empty) o = float4{0.f, 0.f, 0.f, 0.f};
+            else o = float4{o_acc[db][0] * inv, o_acc[db][1] * inv, o_acc[db][2] * inv, o_acc[db][3] * inv};
+            *reinterpret_cast<float4*>(p.out + (static_cast<int64_t>(r) * p.Hq + h) * D + d0) = o;
+        } else {
+            if (empty) o = float4{0.f, 0.f, 0.f, 0.f};
+            else o = float4{o_acc[db][0] * f, o_acc[db][1] * f, o_acc[db][2] * f, o_acc[db][3] * f};
+            *reinterpret_cast<float4*>(p.part_o + pi * D + d0) = o;
+        }
+    }
+    if (split && lg == 0) {
+        p.part_ml[pi * 2 + 0] = nan_run ? __builtin_nanf("") : m_true;
+        p.part_ml[pi * 2 + 1] = bad ? __builtin_nanf("") : (empty ? 0.f : l);
+    }
+    if (p.dbg_visit && lg == 0 && m % G == 0) {
+        int64_t di;
+        if constexpr (MODE == kDecode)
+            di = ((static_cast<int64_t>(b) * p.R + r) * p.Hkv + g) * p.n_slices_max + t_split;
+        else
+            di = (static_cast<int64_t>(r) * p.Hkv + g) * p.n_splits + t_split;
+        p.dbg_visit[di * 3 + 0] = cnt;
+        p.dbg_visit[di * 3 + 1] = sum;
+        p.dbg_visit[di * 3 + 2] = sq;
+    }
+}
+
+template <int MODE, int KT, int D>
+__global__ __launch_bounds__(64, 2) void lean_attn_kernel(MParams p) {
+    extern __shared__ __align__(16) char smem[];
+    __shared__ int s_nids;
+    if constexpr (MODE == kDecode) {
+        const int n_items = decode_items(p);
+        for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+            int t, gy, bz;
+            decode_item(p, item, t, gy, bz);
+            lean_unit<MODE, KT, D>(p, t, gy, bz, smem, s_nids);
+            __syncthreads();
+        }
+    } else {
+        lean_unit<MODE, KT, D>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem, s_nids);
+    }
+}
+
+template <int MODE, int KT, int D>
+int lean_resident_groups(int smem) {
+    static int cached[16] = {0};
+    static int cached_smem[16] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+    if (cached[dev] == 0 || cached_smem[dev] != smem) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lean_attn_kernel<MODE, KT, D>, 64, smem) !=
+                hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        cached[dev] = cus * per_cu;
+        cached_smem[dev] = smem;
+    }
+    return cached[dev];
+}
+
+template <int MODE, int KT, int D>
+hipError_t lean_launch_one(const MParams& p, dim3 grid, hipStream_t st) {
+    const int smem = lean_base_smem<D>() + (MODE == kSel ? p.sel_pow2 * 4 : 0);
+    if constexpr (MODE == kDecode) {
+        const long long items = static_cast<long long>(grid.x) * grid.y * grid.z;
+        const long long n = std::min<long long>(items, lean_resident_groups<MODE, KT, D>(smem));
+        grid = dim3(static_cast<unsigned>(std::max<long long>(n, 1)), 1, 1);
+    }
+    hipLaunchKernelGGL((lean_attn_kernel<MODE, KT, D>), grid, dim3(64), smem, st, p);
+    return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t lean_launch(int dt, const MParams& p, dim3 grid, hipStream_t st) {
+    if (dt == SEL_ATTN_BF16)
+        return p.D == 256 ? lean_launch_one<MODE, SEL_ATTN_BF16, 256>(p, grid, st)
+                          : lean_launch_one<MODE, SEL_ATTN_BF16, 128>(p, grid, st);
+    if (dt == SEL_ATTN_F16)
+        return p.D == 256 ? lean_launch_one<MODE, SEL_ATTN_F16, 256>(p, grid, st)
+                          : lean_launch_one<MODE, SEL_ATTN_F16, 128>(p, grid, st);
+    return p.D == 256 ? lean_launch_one<MODE, SEL_ATTN_I8, 256>(p, grid, st)
+                      : lean_launch_one<MODE, SEL_ATTN_I8, 128>(p, grid, st);
+}
+
+}  // namespace mk
+}  // namespace selattn

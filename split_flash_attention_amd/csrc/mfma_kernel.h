@@ -30,6 +30,8 @@
 #include "common.h"
 #include "internal.h"
 
+#include <algorithm>
+
 namespace selattn {
 namespace mk {
 
@@ -64,6 +66,8 @@ struct MParams {
     const float* mask;
     int64_t m_sr, m_sh;
     int rows_per_wg, n_splits, split_step;
+    // unit grid (x: slices / splits, y: kv heads x query chunks, z: streams / row blocks)
+    int n_units_x, n_units_y, n_units_z;
     // outputs
     float* out;
     float* part_o;
@@ -94,13 +98,20 @@ __device__ __forceinline__ uint32_t i8_to_bf16(uint32_t word, int byte) {
     return __float_as_uint(f) >> 16;
 }
 
-// byte offset of 16-byte chunk `ch` (8 dims) of key row `key` in the K tile
+// byte offset of 16-byte chunk `ch` (8 dims) of key row `key` in the K tile; chunks
+// are XOR-ed with (key & 15) so the 16 rows of one operand read hit distinct banks
 __device__ __forceinline__ int k_off(int key, int ch, int D) {
-    return key * D * 2 + ((ch ^ (key & 7)) << 4);
+    return key * D * 2 + ((ch ^ (key & 15)) << 4);
 }
-// byte offset of contraction chunk `cc` (8 keys) of dim row `d` in the V^T tile
+// byte offset of contraction chunk `cc` (8 keys) of dim row `d` in the V^T tile.
+// Rows are 64 bytes, so four consecutive rows share the 64 LDS banks.  Row d is
+// stored at pr = d ^ ((d >> 3) & 3) and its chunks are XOR-ed with (pr >> 2) & 3:
+// the 16 rows one MFMA operand read touches then fall on distinct 16-byte bank
+// slots, and so do the 32 lanes of a staging write (8 key groups x 4 dim chunks
+// at the same offset within their 8 dims).
 __device__ __forceinline__ int vt_off(int d, int cc) {
-    return d * 64 + ((cc ^ ((d >> 1) & 3)) << 4);
+    const int pr = d ^ ((d >> 3) & 3);
+    return pr * 64 + ((cc ^ ((pr >> 2) & 3)) << 4);
 }
 
 template <int D, bool SEL>
@@ -111,8 +122,11 @@ constexpr int smem_bytes() {
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
+// One work unit: (slice, kv head x query chunk, stream) in decode mode,
+// (split, kv head x query chunk, row block) in prefill modes.
 template <int MODE, int KT, int D, int QB, int W>
-__global__ __launch_bounds__(64 * W) void mfma_attn_kernel(MParams p) {
+__device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, const int gy, const int bz,
+                                          char* smem, int& s_nids) {
     constexpr bool F16 = (KT == SEL_ATTN_F16);
     constexpr bool I8 = (KT == SEL_ATTN_I8);
     constexpr int NKK = D / 32;                  // contraction steps for S^T
@@ -120,19 +134,17 @@ __global__ __launch_bounds__(64 * W) void mfma_attn_kernel(MParams p) {
     constexpr int GCH = I8 ? D / 16 : D / 8;     // 16-byte chunks per K/V row in memory
     constexpr int NT = 64 * W;
     constexpr int K_TASKS = kTK * GCH;           // one 16-byte load each
-    constexpr int V_TASKS = 8 * GCH;             // four 16-byte loads each (4 consecutive keys)
+    constexpr int V_TASKS = 8 * GCH;             // four 16-byte loads each: task e covers
+                                                 // keys 4*(e & 7) + 0..3, chunk e >> 3
     constexpr int NKL = (K_TASKS + NT - 1) / NT;
     constexpr int NVL = (V_TASKS + NT - 1) / NT;
     constexpr int EPC = I8 ? 16 : 8;             // elements per 16-byte chunk
 
-    extern __shared__ __align__(16) char smem[];
     char* k_lds = smem;                                            // kTK * D * 2
     char* vt_lds = smem + kTK * D * 2;                             // D * 64
     float* ksc_lds = reinterpret_cast<float*>(vt_lds + D * 64);    // kTK
     float* vsc_lds = ksc_lds + kTK;                                // kTK
     int* list = reinterpret_cast<int*>(vsc_lds + kTK);             // kMaxSelM (selection)
-
-    __shared__ int s_nids;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -142,18 +154,17 @@ __global__ __launch_bounds__(64 * W) void mfma_attn_kernel(MParams p) {
     const int G = p.G;
 
     // ---- work unit ---------------------------------------------------------
-    const int t_split = blockIdx.x;
-    const int g = blockIdx.y % p.Hkv;
-    const int qchunk = blockIdx.y / p.Hkv;
+    const int g = gy % p.Hkv;
+    const int qchunk = gy / p.Hkv;
     int b = 0, kvl = 0, lo = 0, hi = 0, row0 = 0;
     if constexpr (MODE == kDecode) {
-        b = blockIdx.z;
+        b = bz;
         kvl = min(max(p.kv_len[b], 0), p.cap);
         lo = t_split * p.slice_len;
         if (lo >= kvl) return;            // past this stream's slices: nothing written
         hi = min(lo + p.slice_len, kvl);
     } else {
-        row0 = blockIdx.z * p.rows_per_wg;
+        row0 = bz * p.rows_per_wg;
         lo = t_split * p.split_step;
         hi = min(lo + p.split_step, p.n_kv);
     }
@@ -323,9 +334,9 @@ __global__ __launch_bounds__(64 * W) void mfma_attn_kernel(MParams p) {
             for (int j = 0; j < 4; ++j) {
                 vreg[i][j] = u32x4{0u, 0u, 0u, 0u};
                 if (e < V_TASKS) {
-                    const int cell = slot_cell(t0 + 4 * (e / GCH) + j);
+                    const int cell = slot_cell(t0 + 4 * (e & 7) + j);
                     if (cell >= 0)
-                        vreg[i][j] = *reinterpret_cast<const u32x4*>(vbase + cell * cell_bytes + (e % GCH) * 16);
+                        vreg[i][j] = *reinterpret_cast<const u32x4*>(vbase + cell * cell_bytes + (e >> 3) * 16);
                 }
             }
         }
@@ -365,7 +376,7 @@ __global__ __launch_bounds__(64 * W) void mfma_attn_kernel(MParams p) {
         for (int i = 0; i < NVL; ++i) {
             const int e = tid + i * NT;
             if (e < V_TASKS) {
-                const int kg = e / GCH, ch = e % GCH;
+                const int kg = e & 7, ch = e >> 3;         // key group of 4, 16-byte chunk
                 const int kb = kg >> 2, gq = kg & 3;       // keys kb*16 + 4*gq + j
 #pragma unroll
                 for (int dd = 0; dd < EPC; ++dd) {
@@ -595,6 +606,59 @@ __global__ __launch_bounds__(64 * W) void mfma_attn_kernel(MParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Decode work list.  Only (stream, slice) pairs below a stream's depth hold work;
+// they are numbered densely (stream-major, kv head x query chunk fastest) and a
+// persistent grid takes items w, w + grid, ...  Consecutive work-groups land on
+// different compute units, so the active items spread evenly over the chip
+// whatever the mix of depths (a grid over every possible slice would give some
+// compute units all the slices of one deep stream).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int decode_slices(const MParams& p, int b) {
+    const int n = min(max(p.kv_len[b], 0), p.cap);
+    return min((n + p.slice_len - 1) / p.slice_len, p.n_units_x);
+}
+
+__device__ __forceinline__ int decode_items(const MParams& p) {
+    int n = 0;
+    for (int b = 0; b < p.n_units_z; ++b) n += decode_slices(p, b);
+    return n * p.n_units_y;
+}
+
+__device__ __forceinline__ void decode_item(const MParams& p, int item, int& t, int& gy, int& bz) {
+    const int u = item / p.n_units_y;
+    gy = item - u * p.n_units_y;
+    int base = 0, b = 0;
+    for (; b < p.n_units_z - 1; ++b) {
+        const int ns = decode_slices(p, b);
+        if (u < base + ns) break;
+        base += ns;
+    }
+    bz = b;
+    t = u - base;
+}
+
+// ---------------------------------------------------------------------------
+// the kernel: prefill grids map one work-group to one unit; decode runs the
+// persistent work list above.
+// ---------------------------------------------------------------------------
+template <int MODE, int KT, int D, int QB, int W>
+__global__ __launch_bounds__(64 * W) void mfma_attn_kernel(MParams p) {
+    extern __shared__ __align__(16) char smem[];
+    __shared__ int s_nids;
+    if constexpr (MODE == kDecode) {
+        const int n_items = decode_items(p);
+        for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+            int t, gy, bz;
+            decode_item(p, item, t, gy, bz);
+            attn_unit<MODE, KT, D, QB, W>(p, t, gy, bz, smem, s_nids);
+            __syncthreads();                                         // LDS is reused by the next item
+        }
+    } else {
+        attn_unit<MODE, KT, D, QB, W>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem, s_nids);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launch helpers
 // ---------------------------------------------------------------------------
 struct Shape {
@@ -610,9 +674,33 @@ inline Shape pick_shape(int M) {
     return {3, 4};
 }
 
+// Work-groups of this kernel instance that fit on the device at once (cached per device).
+template <int MODE, int KT, int D, int QB, int W>
+int resident_groups() {
+    static int cached[16] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+    if (cached[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_attn_kernel<MODE, KT, D, QB, W>, 64 * W,
+                                                         smem_bytes<D, MODE == kSel>()) != hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        cached[dev] = cus * per_cu;
+    }
+    return cached[dev];
+}
+
 template <int MODE, int KT, int D, int QB, int W>
 hipError_t launch_one(const MParams& p, dim3 grid, hipStream_t st) {
     constexpr int smem = smem_bytes<D, MODE == kSel>();
+    if constexpr (MODE == kDecode) {
+        const long long items = static_cast<long long>(grid.x) * grid.y * grid.z;
+        const long long n = std::min<long long>(items, resident_groups<MODE, KT, D, QB, W>());
+        grid = dim3(static_cast<unsigned>(std::max<long long>(n, 1)), 1, 1);
+    }
     hipLaunchKernelGGL((mfma_attn_kernel<MODE, KT, D, QB, W>), grid, dim3(64 * W), smem, st, p);
     return hipGetLastError();
 }

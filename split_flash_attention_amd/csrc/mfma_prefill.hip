@@ -4,7 +4,7 @@
 //   message); the row's list is sorted and de-duplicated in LDS first.
 //   Mask mode: one work-group per (block of rows, kv head); rows x heads make up
 //   to 64 query vectors, the F32 mask is read per (row, key).
-#include "mfma_kernel.h"
+#include "lean_kernel.h"
 
 #include <algorithm>
 
@@ -45,6 +45,8 @@ hipError_t launch_mfma_prefill_sel(const sel_attn_prefill_args& a, hipStream_t s
     p.sel = a.sel; p.n_sel = a.n_sel; p.bs = a.block_size; p.sel_pow2 = next_pow2(a.n_sel);
     const int nqc = (p.M + p.qpw - 1) / p.qpw;
     dim3 grid(a.n_splits, a.n_head_kv * nqc, a.n_row);
+    const int64_t span = static_cast<int64_t>(a.n_kv) * a.kv_stride_cell * (a.kv_dtype == SEL_ATTN_I8 ? 1 : 2);
+    if (p.M <= 16 && span < (int64_t{1} << 31) - 64) return lean_launch<kSel>(a.kv_dtype, p, grid, st);
     return launch_mode<kSel>(a.kv_dtype, p, grid, sh, st);
 }
 
