@@ -21,7 +21,6 @@ namespace selattn {
 namespace mk {
 
 constexpr int kLT = 16;          // keys per tile
-constexpr float kLazy = 8.0f;    // slack of the exponent reference, natural units
 
 // K tile: 16 rows of D 16-bit values; 16-byte chunks XOR-ed with (key & 15), so the
 // 16 rows of one operand read land on 16 distinct chunks.
@@ -470,13 +469,10 @@ __global__ __launch_bounds__(64, 2) void lean_attn_kernel(MParams p) {
     extern __shared__ __align__(16) char smem[];
     __shared__ int s_nids;
     if constexpr (MODE == kDecode) {
-        const int n_items = decode_items(p);
-        for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-            int t, gy, bz;
-            decode_item(p, item, t, gy, bz);
+        for_each_decode_item(p, [&](int t, int gy, int bz) {
             lean_unit<MODE, KT, D>(p, t, gy, bz, smem, s_nids);
             __syncthreads();
-        }
+        });
     } else {
         lean_unit<MODE, KT, D>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem, s_nids);
     }
@@ -507,8 +503,7 @@ hipError_t lean_launch_one(const MParams& p, dim3 grid, hipStream_t st) {
     const int smem = lean_base_smem<D>() + (MODE == kSel ? p.sel_pow2 * 4 : 0);
     if constexpr (MODE == kDecode) {
         const long long items = static_cast<long long>(grid.x) * grid.y * grid.z;
-        const long long n = std::min<long long>(items, lean_resident_groups<MODE, KT, D>(smem));
-        grid = dim3(static_cast<unsigned>(std::max<long long>(n, 1)), 1, 1);
+        grid = dim3(decode_grid(items, lean_resident_groups<MODE, KT, D>(smem)), 1, 1);
     }
     hipLaunchKernelGGL((lean_attn_kernel<MODE, KT, D>), grid, dim3(64), smem, st, p);
     return hipGetLastError();

@@ -14,7 +14,7 @@ hipError_t launch_mfma_decode(const sel_attn_decode_args& a, hipStream_t st) {
     p.M = a.n_row * p.G;
     // the single-wave kernel addresses a stream's rows with 32-bit buffer offsets
     const int64_t span = static_cast<int64_t>(a.cap) * a.kv_stride_cell * (a.kv_dtype == SEL_ATTN_I8 ? 1 : 2);
-    const bool lean = p.M <= 16 && span < (int64_t{1} << 31) - 64;
+    const bool lean = span < (int64_t{1} << 31) - 64;
     const Shape sh = lean ? Shape{1, 1} : pick_shape(p.M);
     p.qpw = sh.waves * sh.qb * 16;
     p.q = a.q; p.k = a.k; p.v = a.v;

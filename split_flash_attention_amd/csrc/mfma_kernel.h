@@ -36,6 +36,7 @@ namespace selattn {
 namespace mk {
 
 constexpr int kTK = 32;          // keys per tile
+constexpr float kLazy = 8.0f;    // slack of a lazily moved exponent reference, natural units
 constexpr int kMaxSelM = 4096;   // longest selection list
 
 enum Mode : int { kDecode = 0, kMask = 1, kSel = 2 };
@@ -606,35 +607,54 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
 }
 
 // ---------------------------------------------------------------------------
-// Decode work list.  Only (stream, slice) pairs below a stream's depth hold work;
-// they are numbered densely (stream-major, kv head x query chunk fastest) and a
-// persistent grid takes items w, w + grid, ...  Consecutive work-groups land on
-// different compute units, so the active items spread evenly over the chip
-// whatever the mix of depths (a grid over every possible slice would give some
-// compute units all the slices of one deep stream).
+// Decode work list.  Only (stream, slice) pairs below a stream's depth hold
+// work.  The (stream, slice, kv head) units are numbered densely, unit u goes to
+// XCD u % 8, and the query chunks of a unit are taken by work-groups of that
+// same XCD one after another (work-group w runs on XCD w % 8: dispatch is
+// round-robin over the XCDs), so a unit's K/V slice is fetched into one L2 and
+// shared by its chunks.  A persistent grid (a multiple of 8) walks the list, so
+// the active units spread evenly over the chip whatever the mix of depths.
+// Correctness does not depend on the placement, only locality does.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int decode_slices(const MParams& p, int b) {
     const int n = min(max(p.kv_len[b], 0), p.cap);
     return min((n + p.slice_len - 1) / p.slice_len, p.n_units_x);
 }
 
-__device__ __forceinline__ int decode_items(const MParams& p) {
-    int n = 0;
-    for (int b = 0; b < p.n_units_z; ++b) n += decode_slices(p, b);
-    return n * p.n_units_y;
+// Calls fn(slice, kv head x chunk, stream) for every decode item of this work-group.
+template <typename F>
+__device__ __forceinline__ void for_each_decode_item(const MParams& p, F&& fn) {
+    const int hkv = p.Hkv;
+    const int nqc = p.n_units_y / hkv;
+    int n_su = 0;
+    for (int b = 0; b < p.n_units_z; ++b) n_su += decode_slices(p, b);
+    const int n_u = n_su * hkv;
+    const int xcd = blockIdx.x & 7;
+    const int local = blockIdx.x >> 3;
+    const int lstride = gridDim.x >> 3;
+    const int n_ux = n_u > xcd ? (n_u - xcd + 7) / 8 : 0;
+    const int items = n_ux * nqc;
+    for (int li = local; li < items; li += lstride) {
+        const int uu = li / nqc;
+        const int qc = li - uu * nqc;
+        const int u = uu * 8 + xcd;
+        const int su = u / hkv;
+        const int g = u - su * hkv;
+        int base = 0, b = 0;
+        for (; b < p.n_units_z - 1; ++b) {
+            const int ns = decode_slices(p, b);
+            if (su < base + ns) break;
+            base += ns;
+        }
+        fn(su - base, qc * hkv + g, b);
+    }
 }
 
-__device__ __forceinline__ void decode_item(const MParams& p, int item, int& t, int& gy, int& bz) {
-    const int u = item / p.n_units_y;
-    gy = item - u * p.n_units_y;
-    int base = 0, b = 0;
-    for (; b < p.n_units_z - 1; ++b) {
-        const int ns = decode_slices(p, b);
-        if (u < base + ns) break;
-        base += ns;
-    }
-    bz = b;
-    t = u - base;
+// Persistent decode grid: about one work-group per resident slot, a multiple of 8.
+inline unsigned decode_grid(long long items, int resident) {
+    long long n = std::min<long long>(items, resident);
+    n = std::max<long long>(8, (n / 8) * 8);
+    return static_cast<unsigned>(n);
 }
 
 // ---------------------------------------------------------------------------
@@ -646,13 +666,10 @@ __global__ __launch_bounds__(64 * W) void mfma_attn_kernel(MParams p) {
     extern __shared__ __align__(16) char smem[];
     __shared__ int s_nids;
     if constexpr (MODE == kDecode) {
-        const int n_items = decode_items(p);
-        for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-            int t, gy, bz;
-            decode_item(p, item, t, gy, bz);
+        for_each_decode_item(p, [&](int t, int gy, int bz) {
             attn_unit<MODE, KT, D, QB, W>(p, t, gy, bz, smem, s_nids);
             __syncthreads();                                         // LDS is reused by the next item
-        }
+        });
     } else {
         attn_unit<MODE, KT, D, QB, W>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem, s_nids);
     }
@@ -698,8 +715,7 @@ hipError_t launch_one(const MParams& p, dim3 grid, hipStream_t st) {
     constexpr int smem = smem_bytes<D, MODE == kSel>();
     if constexpr (MODE == kDecode) {
         const long long items = static_cast<long long>(grid.x) * grid.y * grid.z;
-        const long long n = std::min<long long>(items, resident_groups<MODE, KT, D, QB, W>());
-        grid = dim3(static_cast<unsigned>(std::max<long long>(n, 1)), 1, 1);
+        grid = dim3(decode_grid(items, resident_groups<MODE, KT, D, QB, W>()), 1, 1);
     }
     hipLaunchKernelGGL((mfma_attn_kernel<MODE, KT, D, QB, W>), grid, dim3(64 * W), smem, st, p);
     return hipGetLastError();

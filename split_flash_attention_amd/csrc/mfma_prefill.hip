@@ -46,7 +46,11 @@ hipError_t launch_mfma_prefill_sel(const sel_attn_prefill_args& a, hipStream_t s
     const int nqc = (p.M + p.qpw - 1) / p.qpw;
     dim3 grid(a.n_splits, a.n_head_kv * nqc, a.n_row);
     const int64_t span = static_cast<int64_t>(a.n_kv) * a.kv_stride_cell * (a.kv_dtype == SEL_ATTN_I8 ? 1 : 2);
-    if (p.M <= 16 && span < (int64_t{1} << 31) - 64) return lean_launch<kSel>(a.kv_dtype, p, grid, st);
+    if (span < (int64_t{1} << 31) - 64) {
+        p.qpw = 16;
+        const int nqc16 = (p.M + 15) / 16;
+        return lean_launch<kSel>(a.kv_dtype, p, dim3(a.n_splits, a.n_head_kv * nqc16, a.n_row), st);
+    }
     return launch_mode<kSel>(a.kv_dtype, p, grid, sh, st);
 }
 

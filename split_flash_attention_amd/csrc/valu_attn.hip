@@ -395,9 +395,14 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
 // ---------------------------------------------------------------------------
 // split combine
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void combine_kernel(sel_attn_combine_args a) {
+// One 256-thread work-group per (stream, row, head).  A thread owns 4 dims of
+// the output and every nph-th slice (nph = 1024 / D phases), so the slices'
+// partial vectors are read with many independent loads in flight; the phases
+// are then summed through LDS.
+__global__ __launch_bounds__(256) void combine_kernel(sel_attn_combine_args a) {
     const int64_t unit = blockIdx.x;              // (b, r, h)
     const int D = a.head_dim;
+    const int tid = threadIdx.x;
     const int b = static_cast<int>(unit / (static_cast<int64_t>(a.n_row) * a.n_head_q));
     int ns = a.n_slices_max;
     if (a.kv_len) {
@@ -407,33 +412,70 @@ __global__ __launch_bounds__(64) void combine_kernel(sel_attn_combine_args a) {
     const float* ml = a.part_ml + unit * a.n_slices_max * 2;
     const float* po = a.part_o + unit * a.n_slices_max * D;
     float* out = a.out + unit * D;
+
+    __shared__ float s_max[256];
+    __shared__ int s_nan[256];
+    __shared__ float4 s_num[256];
+    __shared__ float s_den[256];
+
+    // M = max over slices (NaN-aware)
     bool nanf = false;
     float M = kNegInf;
-    for (int t = 0; t < ns; ++t) {
+    for (int t = tid; t < ns; t += 256) {
         const float m = ml[2 * t];
         if (m != m) nanf = true;
         else M = max_keep(M, m);
     }
-    const int per = D / 64;                       // 1, 2 or 4 dims per lane
-    const int d0 = threadIdx.x * per;
-    if (nanf || M == kPosInf) {
-        for (int e = 0; e < per; ++e) out[d0 + e] = __builtin_nanf("");
+    s_max[tid] = M;
+    s_nan[tid] = nanf ? 1 : 0;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (tid < off) {
+            s_max[tid] = max_keep(s_max[tid], s_max[tid + off]);
+            s_nan[tid] |= s_nan[tid + off];
+        }
+        __syncthreads();
+    }
+    M = s_max[0];
+    nanf = s_nan[0] != 0;
+
+    const int L = D / 4;                          // float4 columns of a partial
+    const int nph = 256 / L;                      // slice phases
+    const int sp = tid / L, c = tid - (tid / L) * L;
+    if (nanf || M == kPosInf || M == kNegInf) {
+        if (sp == 0) {
+            const float x = (nanf || M == kPosInf) ? __builtin_nanf("") : 0.f;
+            reinterpret_cast<float4*>(out)[c] = float4{x, x, x, x};
+        }
         return;
     }
-    if (M == kNegInf) {
-        for (int e = 0; e < per; ++e) out[d0 + e] = 0.f;
-        return;
-    }
-    float num[4] = {0.f, 0.f, 0.f, 0.f};
+    float4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    for (int t = 0; t < ns; ++t) {
+#pragma unroll 4
+    for (int t = sp; t < ns; t += nph) {
         const float m = ml[2 * t];
         if (m == kNegInf) continue;
         const float w = exp2f((m - M) * kLog2e);
         den = fmaf(w, ml[2 * t + 1], den);
-        for (int e = 0; e < per; ++e) num[e] = fmaf(w, po[static_cast<int64_t>(t) * D + d0 + e], num[e]);
+        const float4 o = reinterpret_cast<const float4*>(po + static_cast<int64_t>(t) * D)[c];
+        num.x = fmaf(w, o.x, num.x);
+        num.y = fmaf(w, o.y, num.y);
+        num.z = fmaf(w, o.z, num.z);
+        num.w = fmaf(w, o.w, num.w);
     }
-    for (int e = 0; e < per; ++e) out[d0 + e] = num[e] / den;
+    s_num[tid] = num;
+    s_den[tid] = den;
+    __syncthreads();
+    if (sp == 0) {
+        float dsum = 0.f;
+        float4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < nph; ++q) {
+            const float4 v = s_num[q * L + c];
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            dsum += s_den[q * L];
+        }
+        reinterpret_cast<float4*>(out)[c] = float4{acc.x / dsum, acc.y / dsum, acc.z / dsum, acc.w / dsum};
+    }
 }
 
 int next_pow2(int x) {
@@ -503,7 +545,7 @@ hipError_t launch_valu_prefill(const sel_attn_prefill_args& a, hipStream_t st) {
 
 hipError_t launch_combine(const sel_attn_combine_args& a, hipStream_t st) {
     const int64_t units = static_cast<int64_t>(a.n_stream) * a.n_row * a.n_head_q;
-    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(units)), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(units)), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
