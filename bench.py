@@ -19,6 +19,7 @@ Prints ONE JSON line.  Inputs are seeded synthetic data (no dataset).
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +30,32 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+# HBM bytes of one decode launch on the split-K workload, from two rocprofv3 --pmc
+# runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
+# by what the same counter reads for the 1 GiB device copy.  The figures describe
+# the kernel sources they were taken on (SHA-256 below); once those change they
+# are stale and `traffic` is reported as null.
+DECODE_TRAFFIC = None
+
+
+def kernel_sources_sha256():
+    """SHA-256 over the HIP sources of the library (file names and contents, sorted)."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "split_flash_attention_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".h", ".hip")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def decode_traffic():
+    t = DECODE_TRAFFIC
+    if t is None or t["sources_sha256"] != kernel_sources_sha256():
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
 
 
 def parse():
@@ -59,8 +86,9 @@ def timed(fn, steps, torch):
     return e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline_decode(wl, streams):
-    """The FP64 oracle (as it stands) on a bounded sample of the decode workload."""
+def cpu_baseline_decode(wl, min_seconds=12.0):
+    """The FP64 oracle (as it stands) on a bounded sample of the decode workload:
+    its streams one at a time, in order, until `min_seconds` have passed."""
     import numpy as np
     import oracle
     try:
@@ -68,17 +96,22 @@ def cpu_baseline_decode(wl, streams):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    sl = slice(0, streams)
+    cells = 0
+    n_calls = 0
     t0 = time.perf_counter()
-    oracle.decode(q=wl.q[sl], k=wl.k[sl], v=wl.v[sl], kv_dtype=wl.kv_dtype, kv_len=wl.kv_len[sl],
-                  causal=wl.causal, scale=wl.scale)
+    while time.perf_counter() - t0 < min_seconds:
+        b = n_calls % wl.n_stream
+        sl = slice(b, b + 1)
+        oracle.decode(q=wl.q[sl], k=wl.k[sl], v=wl.v[sl], kv_dtype=wl.kv_dtype, kv_len=wl.kv_len[sl],
+                      causal=wl.causal, scale=wl.scale)
+        cells += int(wl.kv_len[b])
+        n_calls += 1
     dt = time.perf_counter() - t0
-    cells = int(np.asarray(wl.kv_len[sl], np.int64).sum())
     nbytes = cells * wl.n_head_kv * wl.head_dim * 2 * 2
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"split-K decode workload, streams 0..{streams - 1} ({cells} cells, all 32 heads), "
-                      f"{dt:.1f} s"}
+            "sample": f"split-K decode workload, its first {n_calls} streams in order (cycling), "
+                      f"{cells} cells x 32 heads, {dt:.1f} s"}
 
 
 def main():
@@ -171,8 +204,9 @@ def main():
                    "kv_bytes_per_step": kv_bytes, "decode_path": sa.decode_path(a2),
                    "hbm_peak_frac_step": round(gbs_step / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(gbs_kernel, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs_kernel / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode (mfma_attn_kernel, bf16, D=256)",
+                     "unit": "GB/s", "frac": round(gbs_kernel / HBM_PEAK_GBS, 4),
+                     "traffic": decode_traffic(),
+                     "kernel": "decode (lean_attn_kernel<0, 2, 256>: decode, bf16, D=256)",
                      "kernel_ms": round(ms_decode, 5)},
         "sel_prefill": {"workload": "2048 rows x 512 block ids (4-cell blocks), 16/2 heads, D=256, bf16",
                         "ms": round(ms_prefill, 5), "tflops": round(tflops3, 3),
@@ -208,7 +242,7 @@ def main():
 
     if not args.no_cpu_baseline:
         log("timing the FP64 oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline_decode(wl2, streams=2)
+        result["cpu_baseline"] = cpu_baseline_decode(wl2)
 
     print(json.dumps(result), flush=True)
 

@@ -138,7 +138,8 @@ typedef struct sel_attn_decode_args {
  * kv_len is given, else n_slices_max for every stream.
  * out fp32 [S][R][Hq][D] contiguous.  EINVAL: null part_o/part_ml/out,
  * non-positive sizes, kv_len given with slice_len <= 0 or cap <= 0.
- * EUNSUPPORTED: head_dim not 64/128/256.
+ * EUNSUPPORTED: head_dim not 64/128/256; part_o or out not 16-byte aligned;
+ * part_ml not 8-byte aligned.
  */
 typedef struct sel_attn_combine_args {
     int32_t n_stream, n_row, n_head_q, head_dim;

@@ -70,6 +70,7 @@ int validate_combine(const sel_attn_combine_args* a) {
     if (a->kv_len && (a->slice_len <= 0 || a->cap <= 0)) return SEL_ATTN_EINVAL;
     if (!head_dim_ok(a->head_dim)) return SEL_ATTN_EUNSUPPORTED;
     if (!aligned16(a->part_o) || !aligned16(a->out)) return SEL_ATTN_EUNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(a->part_ml) & 7u) != 0) return SEL_ATTN_EUNSUPPORTED;
     if (static_cast<int64_t>(a->n_stream) * a->n_row * a->n_head_q > 0x7fffffffLL)
         return SEL_ATTN_EUNSUPPORTED;
     return SEL_ATTN_OK;

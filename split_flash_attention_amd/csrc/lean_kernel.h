@@ -40,7 +40,8 @@ constexpr int lean_base_smem() {
     return kLT * D * 2 + D * 32 + 2 * kLT * 4;
 }
 
-template <int MODE, int KT, int D>
+// CP: cache policy of the decode K/V stream loads (0 default, 2 non-temporal).
+template <int MODE, int KT, int D, int CP>
 __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, const int gy, const int bz,
                                           char* smem, int& s_nids) {
     constexpr bool F16 = (KT == SEL_ATTN_F16);
@@ -211,6 +212,10 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), static_cast<short>(0), nrec, 0x00020000);
     constexpr int kAbsent = 0x7ffffff0;        // an offset past any descriptor's end
+    // Cache policy of the decode K/V stream: non-temporal when a unit is read by one
+    // work-group only (the rows are used once and should not displace reusable
+    // lines); the default when several query chunks share it through the L2.
+    constexpr int kStream = CP;
     const int voff_k = (lane / GCH) * cb + (lane % GCH) * 16;            // decode: K task of lane
     const int voff_v = 4 * (lane & 3) * cb + (lane >> 2) * 16;           // decode: V task of lane
 
@@ -228,7 +233,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
             } else {
                 const int off = e < K_TASKS ? voff_k : kAbsent;
                 kreg[i] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, t0 * cb + i * (64 / GCH) * cb, 0));
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, t0 * cb + i * (64 / GCH) * cb, kStream));
             }
         }
 #pragma unroll
@@ -243,7 +248,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                 } else {
                     const int off = e < V_TASKS ? voff_v : kAbsent;
                     vreg[i][j] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, (t0 + j) * cb + 256 * i, 0));
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, (t0 + j) * cb + 256 * i, kStream));
                 }
             }
         }
@@ -464,21 +469,21 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     }
 }
 
-template <int MODE, int KT, int D>
+template <int MODE, int KT, int D, int CP>
 __global__ __launch_bounds__(64, 2) void lean_attn_kernel(MParams p) {
     extern __shared__ __align__(16) char smem[];
     __shared__ int s_nids;
     if constexpr (MODE == kDecode) {
         for_each_decode_item(p, [&](int t, int gy, int bz) {
-            lean_unit<MODE, KT, D>(p, t, gy, bz, smem, s_nids);
+            lean_unit<MODE, KT, D, CP>(p, t, gy, bz, smem, s_nids);
             __syncthreads();
         });
     } else {
-        lean_unit<MODE, KT, D>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem, s_nids);
+        lean_unit<MODE, KT, D, CP>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem, s_nids);
     }
 }
 
-template <int MODE, int KT, int D>
+template <int MODE, int KT, int D, int CP>
 int lean_resident_groups(int smem) {
     static int cached[16] = {0};
     static int cached_smem[16] = {0};
@@ -488,7 +493,7 @@ int lean_resident_groups(int smem) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lean_attn_kernel<MODE, KT, D>, 64, smem) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lean_attn_kernel<MODE, KT, D, CP>, 64, smem) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
@@ -498,27 +503,38 @@ int lean_resident_groups(int smem) {
     return cached[dev];
 }
 
-template <int MODE, int KT, int D>
+template <int MODE, int KT, int D, int CP>
 hipError_t lean_launch_one(const MParams& p, dim3 grid, hipStream_t st) {
     const int smem = lean_base_smem<D>() + (MODE == kSel ? p.sel_pow2 * 4 : 0);
     if constexpr (MODE == kDecode) {
         const long long items = static_cast<long long>(grid.x) * grid.y * grid.z;
-        grid = dim3(decode_grid(items, lean_resident_groups<MODE, KT, D>(smem)), 1, 1);
+        grid = dim3(decode_grid(items, lean_resident_groups<MODE, KT, D, CP>(smem)), 1, 1);
     }
-    hipLaunchKernelGGL((lean_attn_kernel<MODE, KT, D>), grid, dim3(64), smem, st, p);
+    hipLaunchKernelGGL((lean_attn_kernel<MODE, KT, D, CP>), grid, dim3(64), smem, st, p);
     return hipGetLastError();
 }
 
+template <int MODE, int KT, int CP>
+hipError_t lean_launch_dim(const MParams& p, dim3 grid, hipStream_t st) {
+    return p.D == 256 ? lean_launch_one<MODE, KT, 256, CP>(p, grid, st)
+                      : lean_launch_one<MODE, KT, 128, CP>(p, grid, st);
+}
+
+template <int MODE, int CP>
+hipError_t lean_launch_dt(int dt, const MParams& p, dim3 grid, hipStream_t st) {
+    if (dt == SEL_ATTN_BF16) return lean_launch_dim<MODE, SEL_ATTN_BF16, CP>(p, grid, st);
+    if (dt == SEL_ATTN_F16) return lean_launch_dim<MODE, SEL_ATTN_F16, CP>(p, grid, st);
+    return lean_launch_dim<MODE, SEL_ATTN_I8, CP>(p, grid, st);
+}
+
+// Decode streams each unit with non-temporal loads when one work-group reads it
+// (a single query chunk); selection mode and multi-chunk decode keep the default.
 template <int MODE>
 hipError_t lean_launch(int dt, const MParams& p, dim3 grid, hipStream_t st) {
-    if (dt == SEL_ATTN_BF16)
-        return p.D == 256 ? lean_launch_one<MODE, SEL_ATTN_BF16, 256>(p, grid, st)
-                          : lean_launch_one<MODE, SEL_ATTN_BF16, 128>(p, grid, st);
-    if (dt == SEL_ATTN_F16)
-        return p.D == 256 ? lean_launch_one<MODE, SEL_ATTN_F16, 256>(p, grid, st)
-                          : lean_launch_one<MODE, SEL_ATTN_F16, 128>(p, grid, st);
-    return p.D == 256 ? lean_launch_one<MODE, SEL_ATTN_I8, 256>(p, grid, st)
-                      : lean_launch_one<MODE, SEL_ATTN_I8, 128>(p, grid, st);
+    if constexpr (MODE == kDecode) {
+        if (p.n_units_y == p.Hkv) return lean_launch_dt<MODE, 2>(dt, p, grid, st);
+    }
+    return lean_launch_dt<MODE, 0>(dt, p, grid, st);
 }
 
 }  // namespace mk

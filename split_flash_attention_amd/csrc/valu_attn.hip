@@ -395,14 +395,15 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
 // ---------------------------------------------------------------------------
 // split combine
 // ---------------------------------------------------------------------------
-// One 256-thread work-group per (stream, row, head).  A thread owns 4 dims of
-// the output and every nph-th slice (nph = 1024 / D phases), so the slices'
-// partial vectors are read with many independent loads in flight; the phases
-// are then summed through LDS.
-__global__ __launch_bounds__(256) void combine_kernel(sel_attn_combine_args a) {
-    const int64_t unit = blockIdx.x;              // (b, r, h)
+// One wave per (stream, row, head), four per work-group.  Lane c of phase sp owns
+// float4 column c of the output (L = D / 4 columns) and the slices sp, sp + nph,
+// ... (nph = 64 / L phases), so all partial vectors of a row are read with
+// independent loads at once; the phases are then summed by lane exchanges.
+__global__ __launch_bounds__(256) void combine_kernel(sel_attn_combine_args a, int64_t units) {
+    const int64_t unit = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);   // (b, r, h)
+    if (unit >= units) return;                    // uniform over the wave
     const int D = a.head_dim;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int b = static_cast<int>(unit / (static_cast<int64_t>(a.n_row) * a.n_head_q));
     int ns = a.n_slices_max;
     if (a.kv_len) {
@@ -413,35 +414,21 @@ __global__ __launch_bounds__(256) void combine_kernel(sel_attn_combine_args a) {
     const float* po = a.part_o + unit * a.n_slices_max * D;
     float* out = a.out + unit * D;
 
-    __shared__ float s_max[256];
-    __shared__ int s_nan[256];
-    __shared__ float4 s_num[256];
-    __shared__ float s_den[256];
-
     // M = max over slices (NaN-aware)
     bool nanf = false;
     float M = kNegInf;
-    for (int t = tid; t < ns; t += 256) {
+    for (int t = lane; t < ns; t += 64) {
         const float m = ml[2 * t];
         if (m != m) nanf = true;
         else M = max_keep(M, m);
     }
-    s_max[tid] = M;
-    s_nan[tid] = nanf ? 1 : 0;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-        if (tid < off) {
-            s_max[tid] = max_keep(s_max[tid], s_max[tid + off]);
-            s_nan[tid] |= s_nan[tid + off];
-        }
-        __syncthreads();
-    }
-    M = s_max[0];
-    nanf = s_nan[0] != 0;
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) M = max_keep(M, __shfl_xor(M, msk, 64));
+    nanf = __any(nanf);
 
     const int L = D / 4;                          // float4 columns of a partial
-    const int nph = 256 / L;                      // slice phases
-    const int sp = tid / L, c = tid - (tid / L) * L;
+    const int nph = 64 / L;                       // slice phases
+    const int sp = lane / L, c = lane - (lane / L) * L;
     if (nanf || M == kPosInf || M == kNegInf) {
         if (sp == 0) {
             const float x = (nanf || M == kPosInf) ? __builtin_nanf("") : 0.f;
@@ -449,33 +436,42 @@ __global__ __launch_bounds__(256) void combine_kernel(sel_attn_combine_args a) {
         }
         return;
     }
+    // eight slices per round: every load of the round is issued before any is used
     float4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-#pragma unroll 4
-    for (int t = sp; t < ns; t += nph) {
-        const float m = ml[2 * t];
-        if (m == kNegInf) continue;
-        const float w = exp2f((m - M) * kLog2e);
-        den = fmaf(w, ml[2 * t + 1], den);
-        const float4 o = reinterpret_cast<const float4*>(po + static_cast<int64_t>(t) * D)[c];
-        num.x = fmaf(w, o.x, num.x);
-        num.y = fmaf(w, o.y, num.y);
-        num.z = fmaf(w, o.z, num.z);
-        num.w = fmaf(w, o.w, num.w);
-    }
-    s_num[tid] = num;
-    s_den[tid] = den;
-    __syncthreads();
-    if (sp == 0) {
-        float dsum = 0.f;
-        float4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int q = 0; q < nph; ++q) {
-            const float4 v = s_num[q * L + c];
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-            dsum += s_den[q * L];
+    for (int t0 = sp; t0 < ns; t0 += 8 * nph) {
+        float2 mlv[8];
+        float4 ov[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = t0 + j * nph;
+            if (t < ns) {
+                mlv[j] = reinterpret_cast<const float2*>(ml)[t];
+                ov[j] = reinterpret_cast<const float4*>(po + static_cast<int64_t>(t) * D)[c];
+            } else {
+                mlv[j] = float2{kNegInf, 0.f};
+                ov[j] = float4{0.f, 0.f, 0.f, 0.f};
+            }
         }
-        reinterpret_cast<float4*>(out)[c] = float4{acc.x / dsum, acc.y / dsum, acc.z / dsum, acc.w / dsum};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (mlv[j].x == kNegInf) continue;     // empty slice: contributes nothing
+            const float w = exp2f((mlv[j].x - M) * kLog2e);
+            den = fmaf(w, mlv[j].y, den);
+            num.x = fmaf(w, ov[j].x, num.x);
+            num.y = fmaf(w, ov[j].y, num.y);
+            num.z = fmaf(w, ov[j].z, num.z);
+            num.w = fmaf(w, ov[j].w, num.w);
+        }
     }
+    for (int msk = L; msk < 64; msk <<= 1) {
+        num.x += __shfl_xor(num.x, msk, 64);
+        num.y += __shfl_xor(num.y, msk, 64);
+        num.z += __shfl_xor(num.z, msk, 64);
+        num.w += __shfl_xor(num.w, msk, 64);
+        den += __shfl_xor(den, msk, 64);
+    }
+    if (sp == 0) reinterpret_cast<float4*>(out)[c] = float4{num.x / den, num.y / den, num.z / den, num.w / den};
 }
 
 int next_pow2(int x) {
@@ -545,7 +541,7 @@ hipError_t launch_valu_prefill(const sel_attn_prefill_args& a, hipStream_t st) {
 
 hipError_t launch_combine(const sel_attn_combine_args& a, hipStream_t st) {
     const int64_t units = static_cast<int64_t>(a.n_stream) * a.n_row * a.n_head_q;
-    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(units)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((units + 3) / 4)), dim3(256), 0, st, a, units);
     return hipGetLastError();
 }
 

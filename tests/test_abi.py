@@ -154,6 +154,9 @@ def test_prefill_mask_mode_validation(L):
     (dict(n_slices_max=0), sa.EINVAL),
     (dict(kv_len=FAKE, slice_len=0, cap=10), sa.EINVAL),
     (dict(head_dim=32), sa.EUNSUPPORTED),
+    (dict(out=FAKE + 8), sa.EUNSUPPORTED),          # out not 16-byte aligned
+    (dict(part_o=FAKE + 4), sa.EUNSUPPORTED),       # part_o not 16-byte aligned
+    (dict(part_ml=FAKE + 4), sa.EUNSUPPORTED),      # part_ml not 8-byte aligned
 ])
 def test_combine_validation(L, over, code):
     assert _status(L.sel_attn_split_combine, good_combine(**over)) == code
