@@ -1,0 +1,450 @@
+// Matrix-core split-K decode kernel for units with many query vectors: verify
+// windows of R draft rows x G query heads of one kv head (16 x 12 = 192 query
+// vectors per (stream, slice, kv head) unit for the int8 verify workload).
+//
+// One work-group per unit (or per chunk of its query vectors), one wave per block
+// of 16 query vectors, so every K/V tile is loaded, dequantised and staged in LDS
+// once for all query vectors of the unit (TensorFold PR #2595: one work-group per
+// (stream, kv head, slice) of the attn_decode grid; partials merged by the
+// log-sum-exp combine afterwards):
+//   * 32-key tiles: K row-major and V^T in contraction order in LDS (the layouts
+//     of mfma_kernel.h);
+//   * S^T = K . Q^T and O^T += V^T . P^T both on v_mfma_f32_16x16x32, each lane
+//     holding the 8 scores of one query vector that form its P^T operand;
+//   * the tile loads are spread over every thread of the work-group (K as 16-byte
+//     chunks, V as 4 keys x 8 bytes) and kept two tiles ahead in registers;
+//   * lazy rescaling of o and l as in lean_kernel.h: the exponent reference only
+//     moves when a score passes it by more than kLazy, the true maximum is applied
+//     once at the end (the correction exp(m_old - m_new) of TensorFold PR #985,
+//     "What this changes").
+#pragma once
+
+#include "mfma_kernel.h"
+
+namespace selattn {
+namespace mk {
+
+// LDS: K tile, V^T tile, the tile's int8 scales, and each wave's Q^T operands
+// (16 query vectors x D, bf16/fp16, in operand order).
+template <int D, int W>
+constexpr int group_smem() {
+    return kTK * D * 2 + D * 64 + 2 * kTK * 4 + W * D * 32;
+}
+
+template <int KT, int D, int W>
+__device__ __forceinline__ void group_unit(const MParams& p, const int t_split, const int gy, const int b,
+                                           char* smem) {
+    constexpr bool F16 = (KT == SEL_ATTN_F16);
+    constexpr bool I8 = (KT == SEL_ATTN_I8);
+    constexpr int NKK = D / 32;                  // contraction steps of S^T
+    constexpr int NDB = D / 16;                  // dim blocks of O^T
+    constexpr int GCH = I8 ? D / 16 : D / 8;     // 16-byte chunks per K/V row in memory
+    constexpr int NT = 64 * W;
+    constexpr int K_TASKS = kTK * GCH;           // task e < K_TASKS: K row e / GCH, chunk e % GCH
+    constexpr int V_TASKS = 8 * 2 * GCH;         // keys 4 * (e' & 7) + 0..3, 8-byte half chunk e' >> 3
+    constexpr int TASKS = K_TASKS + V_TASKS;
+    constexpr int NSLOT = (TASKS + NT - 1) / NT;
+    constexpr int EPH = I8 ? 8 : 4;              // elements per 8-byte half chunk
+    constexpr int ROWB = D * (I8 ? 1 : 2);
+    static_assert(K_TASKS % 64 == 0 && V_TASKS % 64 == 0, "tasks must fill whole waves");
+
+    char* k_lds = smem;                                            // kTK * D * 2
+    char* vt_lds = smem + kTK * D * 2;                             // D * 64
+    float* ksc_lds = reinterpret_cast<float*>(vt_lds + D * 64);    // kTK
+    float* vsc_lds = ksc_lds + kTK;                                // kTK
+    char* q_lds = reinterpret_cast<char*>(vsc_lds + kTK);          // W * D * 32
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    const int G = p.G;
+
+    // ---- work unit ---------------------------------------------------------
+    const int g = gy % p.Hkv;
+    const int qchunk = gy / p.Hkv;
+    const int kvl = min(max(p.kv_len[b], 0), p.cap);
+    const int lo = t_split * p.slice_len;
+    if (lo >= kvl) return;                      // uniform over the work-group
+    const int hi = min(lo + p.slice_len, kvl);
+    const int m_wg = qchunk * p.qpw;
+    const int m_end = min(p.M, m_wg + p.qpw);
+    const int m_wave = m_wg + wave * 16;
+    const bool wave_live = m_wave < m_end;      // uniform over the wave
+
+    // this lane's query vector: row r, head h
+    const int m = m_wave + ln;
+    bool ok = m < m_end;
+    int r = m / G, h = g * G + m % G;
+    ok = ok && r < p.R;
+    if (!ok) { r = 0; h = g * G; }
+    const int pos = kvl - p.R + r;
+    int lim = min(p.causal ? min(pos + 1, kvl) : kvl, hi);
+    if (!ok) lim = -1;
+
+    // Q^T operands, scale folded in, kept in this wave's part of LDS (registers go
+    // to the O^T accumulators): step kk of lane l at kk * 1024 + l * 16
+    char* qw_lds = q_lds + wave * (NKK * 1024) + lane * 16;
+    {
+        const float* qp = p.q + ((static_cast<int64_t>(b) * p.R + r) * p.Hq + h) * D;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            float x[8];
+            if (ok) {
+                const float4 a = *reinterpret_cast<const float4*>(qp + kk * 32 + 8 * lg);
+                const float4 c = *reinterpret_cast<const float4*>(qp + kk * 32 + 8 * lg + 4);
+                x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+                x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = 0.f;
+            }
+            u32x4 qv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qv[j] = pack2<F16>(x[2 * j] * p.scale, x[2 * j + 1] * p.scale);
+            *reinterpret_cast<u32x4*>(qw_lds + kk * 1024) = qv;
+        }
+    }
+    const float slope = (p.alibi && ok) ? p.alibi[h] : 0.f;
+
+    // keys no query vector of the work-group can see are never loaded
+    int lim_max = -1;
+    for (int rr = m_wg / G; rr <= (m_end - 1) / G && rr < p.R; ++rr)
+        lim_max = max(lim_max, p.causal ? min(kvl - p.R + rr + 1, kvl) : kvl);
+    const int n_keys = max(0, min(hi, lim_max) - lo);
+
+    // ---- tile loads ----------------------------------------------------------
+    // Buffer loads through a descriptor that starts at the unit's first key row and
+    // ends with its last needed row: rows past it (the tail of the last tile) read
+    // as zeros.  32-bit offsets: slice_len * cell stride < 2^31 is checked on the host.
+    const int cb = static_cast<int>(p.kv_sc * (I8 ? 1 : 2));
+    const int64_t kv_base = static_cast<int64_t>(b) * p.kv_ss + static_cast<int64_t>(g) * p.kv_sh;
+    const int64_t sc_base = static_cast<int64_t>(b) * p.sc_ss + static_cast<int64_t>(g) * p.sc_sh;
+    const char* kbase = static_cast<const char*>(p.k) + (kv_base + static_cast<int64_t>(lo) * p.kv_sc) * (I8 ? 1 : 2);
+    const char* vbase = static_cast<const char*>(p.v) + (kv_base + static_cast<int64_t>(lo) * p.kv_sc) * (I8 ? 1 : 2);
+    const int nrec = n_keys > 0 ? (n_keys - 1) * cb + ROWB : 0;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), static_cast<short>(0), nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), static_cast<short>(0), nrec, 0x00020000);
+
+    // slot i of thread tid holds task tid + i * NT: a K chunk in k[i], or four
+    // 8-byte V pieces in v[i][0].xy, v[i][0].zw, v[i][1].xy, v[i][1].zw
+    struct Regs {
+        u32x4 k[NSLOT];
+        u32x4 v[NSLOT][2];
+        float ks, vs;
+    };
+    // (K and V slots are filled in separate passes, so no store is shared between
+    // the two kinds and the slots stay in registers)
+    auto load_tile = [&](Regs& rg, int t0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NSLOT; ++i) {
+            const int e = tid + i * NT;
+            if (e < K_TASKS) {
+                const int voff = (e / GCH) * cb + (e % GCH) * 16;
+                rg.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, t0 * cb, 0));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NSLOT; ++i) {
+            const int e = tid + i * NT;
+            if (e >= K_TASKS && e < TASKS) {
+                const int ev = e - K_TASKS;
+                const int voff = 4 * (ev & 7) * cb + (ev >> 3) * 8;
+                const u32x2 a0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, voff, t0 * cb, 0));
+                const u32x2 a1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, voff, (t0 + 1) * cb, 0));
+                const u32x2 a2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, voff, (t0 + 2) * cb, 0));
+                const u32x2 a3 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, voff, (t0 + 3) * cb, 0));
+                rg.v[i][0] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                rg.v[i][1] = u32x4{a2[0], a2[1], a3[0], a3[1]};
+            }
+        }
+        if constexpr (I8) {
+            if (tid < kTK) {
+                const bool in = t0 + tid < n_keys;
+                const int64_t si = sc_base + static_cast<int64_t>(lo + t0 + tid) * p.sc_sc;
+                rg.ks = in ? p.ksc[si] : 0.f;
+                rg.vs = in ? p.vsc[si] : 0.f;
+            }
+        }
+    };
+    auto store_tile = [&](const Regs& rg) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NSLOT; ++i) {
+            const int e = tid + i * NT;
+            if (e < K_TASKS) {
+                const int key = e / GCH, ch = e % GCH;
+                if constexpr (I8) {
+                    const u32x4 rw = rg.k[i];
+                    u32x4 w0, w1;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        w0[2 * j] = i8_to_bf16(rw[j], 0) | (i8_to_bf16(rw[j], 1) << 16);
+                        w0[2 * j + 1] = i8_to_bf16(rw[j], 2) | (i8_to_bf16(rw[j], 3) << 16);
+                        w1[2 * j] = i8_to_bf16(rw[2 + j], 0) | (i8_to_bf16(rw[2 + j], 1) << 16);
+                        w1[2 * j + 1] = i8_to_bf16(rw[2 + j], 2) | (i8_to_bf16(rw[2 + j], 3) << 16);
+                    }
+                    *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch, D)) = w0;
+                    *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch + 1, D)) = w1;
+                } else {
+                    *reinterpret_cast<u32x4*>(k_lds + k_off(key, ch, D)) = rg.k[i];
+                }
+            } else if (e < TASKS) {
+                const int ev = e - K_TASKS;
+                const int kg = ev & 7, hc = ev >> 3;        // keys 4 * kg + j, half chunk hc
+                const int kb = kg >> 2, gq = kg & 3;        // keys kb * 16 + 4 * gq + j
+                // the 8 bytes of key j: word pair (x[j >> 1] lanes 2 * (j & 1) + 0..1)
+                uint32_t w[4][2];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    w[j][0] = rg.v[i][j >> 1][2 * (j & 1)];
+                    w[j][1] = rg.v[i][j >> 1][2 * (j & 1) + 1];
+                }
+#pragma unroll
+                for (int dd = 0; dd < EPH; ++dd) {
+                    uint32_t lo2, hi2;
+                    if constexpr (I8) {
+                        const int wi = dd >> 2, by = dd & 3;
+                        lo2 = i8_to_bf16(w[0][wi], by) | (i8_to_bf16(w[1][wi], by) << 16);
+                        hi2 = i8_to_bf16(w[2][wi], by) | (i8_to_bf16(w[3][wi], by) << 16);
+                    } else {
+                        const int wi = dd >> 1;
+                        if (dd & 1) {
+                            lo2 = (w[0][wi] >> 16) | (w[1][wi] & 0xffff0000u);
+                            hi2 = (w[2][wi] >> 16) | (w[3][wi] & 0xffff0000u);
+                        } else {
+                            lo2 = (w[0][wi] & 0xffffu) | (w[1][wi] << 16);
+                            hi2 = (w[2][wi] & 0xffffu) | (w[3][wi] << 16);
+                        }
+                    }
+                    *reinterpret_cast<uint2*>(vt_lds + vt_off(hc * EPH + dd, gq) + 8 * kb) = uint2{lo2, hi2};
+                }
+            }
+        }
+        if constexpr (I8) {
+            if (tid < kTK) {
+                ksc_lds[tid] = rg.ks;
+                vsc_lds[tid] = rg.vs;
+            }
+        }
+    };
+
+    // ---- running state ---------------------------------------------------------
+    float m_use = kNegInf;     // exponent reference of o and l
+    float m_true = kNegInf;    // largest visible non-NaN score seen
+    float l_run = 0.f;
+    bool nan_run = false;
+    long long dbg_cnt = 0, dbg_sum = 0, dbg_sq = 0;
+    f32x4 o_acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // one tile of math on the staged K/V (the caller brackets it with barriers)
+    auto tile_math = [&](int t0) __attribute__((always_inline)) {
+        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const u32x4 qk = *reinterpret_cast<const u32x4*>(qw_lds + kk * 1024);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(k_lds + k_off(kb * 16 + ln, kk * 4 + lg, D));
+                s[kb] = mfma16x16x32<F16>(a, qk, s[kb]);
+            }
+        }
+        float sc[8];
+        bool vis[8];
+        float tmax = kNegInf;
+        bool tnan = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int kb = e >> 2, i = e & 3;
+            const int cell = lo + t0 + kb * 16 + 4 * lg + i;
+            const bool v = cell < lim;
+            float x = s[kb][i];
+            if constexpr (I8) x *= ksc_lds[kb * 16 + 4 * lg + i];
+            if (p.softcap > 0.f) x = p.softcap * tanhf(x / p.softcap);
+            x += slope * static_cast<float>(cell - pos);
+            vis[e] = v;
+            sc[e] = x;
+            if (v) {
+                if (x != x) tnan = true;
+                else tmax = max_keep(tmax, x);
+            }
+            if (p.dbg_visit && v) {
+                dbg_cnt += 1;
+                dbg_sum += cell;
+                dbg_sq += static_cast<long long>(cell) * cell;
+            }
+        }
+        tmax = max_keep(tmax, wave_xor(tmax, 16));
+        tmax = max_keep(tmax, wave_xor(tmax, 32));
+        int tn = tnan ? 1 : 0;
+        tn |= wave_xor_i(tn, 16);
+        tn |= wave_xor_i(tn, 32);
+        nan_run = nan_run || tn;
+        m_true = max_keep(m_true, tmax);
+        const bool need = (tmax > m_use + kLazy) || (m_use == kNegInf && tmax != kNegInf);
+        if (wave_any(need)) {
+            const float c = need ? rescale_factor(m_use, tmax) : 1.f;
+            if (need) m_use = tmax;
+            l_run *= c;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o_acc[db] *= c;
+        }
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float w = vis[e] ? exp_diff(sc[e], m_use) : 0.f;
+            l_run += w;
+            pv[e] = w;
+            if constexpr (I8) pv[e] *= vsc_lds[(e >> 2) * 16 + 4 * lg + (e & 3)];
+        }
+        const u32x4 pop = u32x4{pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]),
+                                pack2<F16>(pv[4], pv[5]), pack2<F16>(pv[6], pv[7])};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(vt_lds + vt_off(db * 16 + ln, lg));
+            o_acc[db] = mfma16x16x32<F16>(a, pop, o_acc[db]);
+        }
+    };
+
+    // two register sets: the loads of tile t + 2 are in flight during tiles t and t + 1
+    Regs ra, rb;
+    if (n_keys > 0) load_tile(ra, 0);
+    if (n_keys > kTK) load_tile(rb, kTK);
+    for (int t0 = 0; t0 < n_keys; t0 += 2 * kTK) {
+        store_tile(ra);
+        __syncthreads();
+        if (t0 + 2 * kTK < n_keys) load_tile(ra, t0 + 2 * kTK);
+        if (wave_live) tile_math(t0);
+        __syncthreads();
+        if (t0 + kTK < n_keys) {
+            store_tile(rb);
+            __syncthreads();
+            if (t0 + 3 * kTK < n_keys) load_tile(rb, t0 + 3 * kTK);
+            if (wave_live) tile_math(t0 + kTK);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: partials of this slice -------------------------------------
+    if (!wave_live) return;
+    float l = l_run;
+    l += wave_xor(l, 16);
+    l += wave_xor(l, 32);
+    long long cnt = 0, sum = 0, sq = 0;
+    if (p.dbg_visit) {
+        auto xsum = [&](long long v) -> long long {
+            long long acc = v;
+            for (int msk = 16; msk <= 32; msk <<= 1) {
+                const unsigned lo32 = static_cast<unsigned>(acc & 0xffffffffLL);
+                const int hi32 = static_cast<int>(acc >> 32);
+                const unsigned olo = static_cast<unsigned>(wave_xor_i(static_cast<int>(lo32), msk));
+                const int ohi = wave_xor_i(hi32, msk);
+                acc += static_cast<long long>(
+                    (static_cast<unsigned long long>(static_cast<unsigned>(ohi)) << 32) | olo);
+            }
+            return acc;
+        };
+        cnt = xsum(dbg_cnt);
+        sum = xsum(dbg_sum);
+        sq = xsum(dbg_sq);
+    }
+    if (!ok) return;
+    const bool bad = nan_run || m_true == kPosInf;
+    const bool empty = !bad && m_true == kNegInf;
+    float f = 1.f;
+    if (!bad && !empty && m_use != m_true) f = exp2f((m_use - m_true) * kLog2e);
+    l *= f;
+    const int64_t pi = ((static_cast<int64_t>(b) * p.R + r) * p.Hq + h) * p.n_slices_max + t_split;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int d0 = db * 16 + 4 * lg;
+        float4 o;
+        if (empty) o = float4{0.f, 0.f, 0.f, 0.f};
+        else o = float4{o_acc[db][0] * f, o_acc[db][1] * f, o_acc[db][2] * f, o_acc[db][3] * f};
+        *reinterpret_cast<float4*>(p.part_o + pi * D + d0) = o;
+    }
+    if (lg == 0) {
+        p.part_ml[pi * 2 + 0] = nan_run ? __builtin_nanf("") : m_true;
+        p.part_ml[pi * 2 + 1] = bad ? __builtin_nanf("") : (empty ? 0.f : l);
+    }
+    if (p.dbg_visit && lg == 0 && m % G == 0) {
+        const int64_t di = ((static_cast<int64_t>(b) * p.R + r) * p.Hkv + g) * p.n_slices_max + t_split;
+        p.dbg_visit[di * 3 + 0] = cnt;
+        p.dbg_visit[di * 3 + 1] = sum;
+        p.dbg_visit[di * 3 + 2] = sq;
+    }
+}
+
+template <int KT, int D, int W>
+__global__ __launch_bounds__(64 * W) void group_decode_kernel(MParams p) {
+    extern __shared__ __align__(16) char smem[];
+    for_each_decode_item(p, [&](int t, int gy, int bz) {
+        group_unit<KT, D, W>(p, t, gy, bz, smem);
+        __syncthreads();                                         // LDS is reused by the next item
+    });
+}
+
+// ---------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------
+// Waves per work-group for nqb blocks of 16 query vectors (nqb >= 2): 4, 8 or 12,
+// the fewest idle waves; more than 12 blocks are cut into query chunks.
+inline int group_waves(int nqb) {
+    if (nqb <= 4) return 4;
+    if (nqb <= 8) return 8;
+    if (nqb <= 12) return 12;
+    const int c8 = (nqb + 7) / 8 * 8, c12 = (nqb + 11) / 12 * 12;
+    return c12 <= c8 ? 12 : 8;
+}
+
+template <int KT, int D, int W>
+hipError_t group_launch_one(const MParams& p, dim3 grid, hipStream_t st) {
+    constexpr int smem = group_smem<D, W>();
+    static int cached[16] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+    if (cached[dev] == 0) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&group_decode_kernel<KT, D, W>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+        if (e != hipSuccess) return e;
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, group_decode_kernel<KT, D, W>, 64 * W, smem) !=
+                hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        cached[dev] = cus * per_cu;
+    }
+    const long long items = static_cast<long long>(grid.x) * grid.y * grid.z;
+    hipLaunchKernelGGL((group_decode_kernel<KT, D, W>), dim3(decode_grid(items, cached[dev])), dim3(64 * W), smem,
+                       st, p);
+    return hipGetLastError();
+}
+
+template <int KT, int D>
+hipError_t group_launch_w(const MParams& p, dim3 grid, int w, hipStream_t st) {
+    switch (w) {
+    case 4: return group_launch_one<KT, D, 4>(p, grid, st);
+    case 8: return group_launch_one<KT, D, 8>(p, grid, st);
+    default: return group_launch_one<KT, D, 12>(p, grid, st);
+    }
+}
+
+inline hipError_t group_launch(int dt, const MParams& p, dim3 grid, int w, hipStream_t st) {
+    if (dt == SEL_ATTN_BF16)
+        return p.D == 256 ? group_launch_w<SEL_ATTN_BF16, 256>(p, grid, w, st)
+                          : group_launch_w<SEL_ATTN_BF16, 128>(p, grid, w, st);
+    if (dt == SEL_ATTN_F16)
+        return p.D == 256 ? group_launch_w<SEL_ATTN_F16, 256>(p, grid, w, st)
+                          : group_launch_w<SEL_ATTN_F16, 128>(p, grid, w, st);
+    return p.D == 256 ? group_launch_w<SEL_ATTN_I8, 256>(p, grid, w, st)
+                      : group_launch_w<SEL_ATTN_I8, 128>(p, grid, w, st);
+}
+
+}  // namespace mk
+}  // namespace selattn

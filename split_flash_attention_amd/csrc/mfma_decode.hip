@@ -1,6 +1,9 @@
-// Split-K decode and verify windows on the matrix-core kernel: one work-group
+// Split-K decode and verify windows on the matrix-core kernels: one work-group
 // per (stream, kv head, slice[, query chunk]) (TensorFold PR #2595: the
 // attn_decode grid of rows, heads and slices), partials merged by the combine.
+// Up to 16 query vectors per unit run on the single-wave kernel, more on the
+// group kernel (one wave per 16 query vectors sharing each K/V tile).
+#include "group_kernel.h"
 #include "lean_kernel.h"
 
 #include <algorithm>
@@ -12,11 +15,6 @@ hipError_t launch_mfma_decode(const sel_attn_decode_args& a, hipStream_t st) {
     MParams p{};
     p.Hq = a.n_head_q; p.Hkv = a.n_head_kv; p.G = a.n_head_q / a.n_head_kv; p.D = a.head_dim;
     p.M = a.n_row * p.G;
-    // the single-wave kernel addresses a stream's rows with 32-bit buffer offsets
-    const int64_t span = static_cast<int64_t>(a.cap) * a.kv_stride_cell * (a.kv_dtype == SEL_ATTN_I8 ? 1 : 2);
-    const bool lean = span < (int64_t{1} << 31) - 64;
-    const Shape sh = lean ? Shape{1, 1} : pick_shape(p.M);
-    p.qpw = sh.waves * sh.qb * 16;
     p.q = a.q; p.k = a.k; p.v = a.v;
     p.kv_ss = a.kv_stride_stream; p.kv_sc = a.kv_stride_cell; p.kv_sh = a.kv_stride_head;
     p.ksc = a.k_scale; p.vsc = a.v_scale;
@@ -25,14 +23,32 @@ hipError_t launch_mfma_decode(const sel_attn_decode_args& a, hipStream_t st) {
     p.R = a.n_row; p.cap = a.cap; p.kv_len = a.kv_len; p.causal = a.causal;
     p.slice_len = a.slice_len; p.n_slices_max = a.n_slices_max;
     p.part_o = a.part_o; p.part_ml = a.part_ml; p.dbg_visit = a.dbg_visit;
-    const int nqc = (p.M + p.qpw - 1) / p.qpw;
     const int n_sl = std::min(a.n_slices_max, (a.cap + a.slice_len - 1) / a.slice_len);
     p.n_units_x = n_sl;
-    p.n_units_y = a.n_head_kv * nqc;
     p.n_units_z = a.n_stream;
-    dim3 grid(n_sl, a.n_head_kv * nqc, a.n_stream);
-    if (lean) return lean_launch<kDecode>(a.kv_dtype, p, grid, st);
-    return launch_mode<kDecode>(a.kv_dtype, p, grid, sh, st);
+    // the single-wave and group kernels address a unit's rows with 32-bit buffer offsets
+    const int64_t cell_bytes = a.kv_stride_cell * (a.kv_dtype == SEL_ATTN_I8 ? 1 : 2);
+    const bool off32 = static_cast<int64_t>(a.cap) * cell_bytes < (int64_t{1} << 31) - 64;
+    const int nqb = (p.M + 15) / 16;
+    if (off32 && nqb <= 1) {
+        // one block of 16 query vectors: one wave per unit
+        p.qpw = 16;
+        p.n_units_y = a.n_head_kv;
+        return lean_launch<kDecode>(a.kv_dtype, p, dim3(n_sl, a.n_head_kv, a.n_stream), st);
+    }
+    if (off32) {
+        // many query vectors: one wave per block, a work-group shares each tile
+        const int w = group_waves(nqb);
+        p.qpw = 16 * w;
+        const int nqc = (nqb + w - 1) / w;
+        p.n_units_y = a.n_head_kv * nqc;
+        return group_launch(a.kv_dtype, p, dim3(n_sl, a.n_head_kv * nqc, a.n_stream), w, st);
+    }
+    const Shape sh = pick_shape(p.M);
+    p.qpw = sh.waves * sh.qb * 16;
+    const int nqc = (p.M + p.qpw - 1) / p.qpw;
+    p.n_units_y = a.n_head_kv * nqc;
+    return launch_mode<kDecode>(a.kv_dtype, p, dim3(n_sl, a.n_head_kv * nqc, a.n_stream), sh, st);
 }
 
 }  // namespace selattn

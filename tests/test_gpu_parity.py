@@ -88,6 +88,18 @@ DECODE_CASES = {
     "bf16_noncausal_d128": dict(n_stream=2, n_row=3, n_head_q=4, n_head_kv=1, head_dim=128,
                                 cap=300, kv_dtype="bf16", depths=[300, 65], slice_len=64,
                                 causal=False),
+    # more than 16 query vectors per unit: the work-group kernel with 4, 8 and 12
+    # waves, a partly filled last block, and two query chunks per unit
+    "bf16_verify_w4_d128": dict(n_stream=2, n_row=5, n_head_q=16, n_head_kv=2, head_dim=128,
+                                cap=1500, kv_dtype="bf16", depths=[1500, 37], slice_len=512),
+    "f16_verify_w8_softcap_alibi": dict(n_stream=2, n_row=16, n_head_q=8, n_head_kv=1, head_dim=256,
+                                        cap=700, kv_dtype="f16", depths=[700, 300], slice_len=256,
+                                        softcap=20.0, alibi=True),
+    "bf16_verify_two_chunks": dict(n_stream=2, n_row=16, n_head_q=16, n_head_kv=1, head_dim=256,
+                                   cap=600, kv_dtype="bf16", depths=[600, 100], slice_len=256),
+    "i8_verify_noncausal_d128": dict(n_stream=2, n_row=7, n_head_q=24, n_head_kv=2, head_dim=128,
+                                     cap=900, kv_dtype="i8", depths=[900, 250], slice_len=384,
+                                     causal=False),
 }
 
 
