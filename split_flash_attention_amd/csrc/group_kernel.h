@@ -24,11 +24,11 @@
 namespace selattn {
 namespace mk {
 
-// LDS: K tile, V^T tile, the tile's int8 scales, and each wave's Q^T operands
-// (16 query vectors x D, bf16/fp16, in operand order).
+// LDS: K tile, V^T tile, the tile's int8 scales, each wave's Q^T operands (16
+// query vectors x D, bf16/fp16, in operand order) and its visit counters.
 template <int D, int W>
 constexpr int group_smem() {
-    return kTK * D * 2 + D * 64 + 2 * kTK * 4 + W * D * 32;
+    return kTK * D * 2 + D * 64 + 2 * kTK * 4 + W * D * 32 + W * 16 * 3 * 8;
 }
 
 template <int KT, int D, int W>
@@ -53,6 +53,8 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     float* ksc_lds = reinterpret_cast<float*>(vt_lds + D * 64);    // kTK
     float* vsc_lds = ksc_lds + kTK;                                // kTK
     char* q_lds = reinterpret_cast<char*>(vsc_lds + kTK);          // W * D * 32
+    unsigned long long* dbg_lds =                                  // W * 16 * 3
+        reinterpret_cast<unsigned long long*>(q_lds + W * D * 32);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -202,14 +204,28 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                     w[j][0] = rg.v[i][j >> 1][2 * (j & 1)];
                     w[j][1] = rg.v[i][j >> 1][2 * (j & 1) + 1];
                 }
+                if constexpr (I8) {
+                    // dims hc * 8 + 4 * h + jj (byte jj of word h of each key).  Their
+                    // V^T rows are hc * 8 + 4 * h + (jj ^ c), c = hc & 3, and the chunk
+                    // swizzle depends on h only: the address is a per-half base with
+                    // (jj ^ c) in bits 6..7, i.e. (base + (c << 6)) ^ (jj << 6).  Lanes
+                    // with different c land in different bank quarters at each step.
+                    const int c = hc & 3;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int wbc = (hc * 8 + 4 * h + c) * 64 + ((gq ^ ((2 * hc + h) & 3)) << 4) + 8 * kb;
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const uint32_t lo2 = i8_to_bf16(w[0][h], jj) | (i8_to_bf16(w[1][h], jj) << 16);
+                            const uint32_t hi2 = i8_to_bf16(w[2][h], jj) | (i8_to_bf16(w[3][h], jj) << 16);
+                            *reinterpret_cast<uint2*>(vt_lds + (wbc ^ (jj << 6))) = uint2{lo2, hi2};
+                        }
+                    }
+                } else {
 #pragma unroll
                 for (int dd = 0; dd < EPH; ++dd) {
                     uint32_t lo2, hi2;
-                    if constexpr (I8) {
-                        const int wi = dd >> 2, by = dd & 3;
-                        lo2 = i8_to_bf16(w[0][wi], by) | (i8_to_bf16(w[1][wi], by) << 16);
-                        hi2 = i8_to_bf16(w[2][wi], by) | (i8_to_bf16(w[3][wi], by) << 16);
-                    } else {
+                    {
                         const int wi = dd >> 1;
                         if (dd & 1) {
                             lo2 = (w[0][wi] >> 16) | (w[1][wi] & 0xffff0000u);
@@ -220,6 +236,7 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                         }
                     }
                     *reinterpret_cast<uint2*>(vt_lds + vt_off(hc * EPH + dd, gq) + 8 * kb) = uint2{lo2, hi2};
+                }
                 }
             }
         }
@@ -236,10 +253,26 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     float m_true = kNegInf;    // largest visible non-NaN score seen
     float l_run = 0.f;
     bool nan_run = false;
-    long long dbg_cnt = 0, dbg_sum = 0, dbg_sq = 0;
+    // visit counters of this lane's query vector (count, sum, sum of squares of
+    // the cells it combines) live in LDS, so they hold no registers in the loop
+    unsigned long long* my_dbg = dbg_lds + (wave * 16 + ln) * 3;
+    if (p.dbg_visit && lg == 0) my_dbg[0] = my_dbg[1] = my_dbg[2] = 0ull;
     f32x4 o_acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Operand read addresses written as base + immediate offset.  K (k_off): key
+    // kb * 16 + ln, chunk kk * 4 + lg, XOR-ed with ln, which only touches the low two
+    // bits of kk: four bases.  V^T (vt_off): dim db * 16 + ln, chunk lg; the row XOR
+    // depends on db & 1 only and the chunk XOR not on db: two bases.
+    int kread[4], vread[2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kread[q] = ln * D * 2 + (((q * 4 + lg) ^ ln) << 4);
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        const int x = (2 * par + (ln >> 3)) & 3;
+        vread[par] = (ln ^ x) * 64 + ((lg ^ ((ln >> 2) & 3)) << 4);
+    }
 
     // one tile of math on the staged K/V (the caller brackets it with barriers)
     auto tile_math = [&](int t0) __attribute__((always_inline)) {
@@ -249,42 +282,61 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
             const u32x4 qk = *reinterpret_cast<const u32x4*>(qw_lds + kk * 1024);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(k_lds + k_off(kb * 16 + ln, kk * 4 + lg, D));
+                const u32x4 a = *reinterpret_cast<const u32x4*>(k_lds + kread[kk & 3] + (kk >> 2) * 256 + kb * 16 * D * 2);
                 s[kb] = mfma16x16x32<F16>(a, qk, s[kb]);
             }
         }
+        // score e of this lane is key cell0 + off(e): off = (e >> 2) * 16 + (e & 3)
+        const int cell0 = lo + t0 + 4 * lg;
+        const int vlim = lim - cell0;               // visible iff off(e) < vlim
         float sc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[e] = s[e >> 2][e & 3];
+        if constexpr (I8) {
+            const float4 k0 = *reinterpret_cast<const float4*>(ksc_lds + 4 * lg);
+            const float4 k1 = *reinterpret_cast<const float4*>(ksc_lds + 16 + 4 * lg);
+            sc[0] *= k0.x; sc[1] *= k0.y; sc[2] *= k0.z; sc[3] *= k0.w;
+            sc[4] *= k1.x; sc[5] *= k1.y; sc[6] *= k1.z; sc[7] *= k1.w;
+        }
+        if (p.softcap > 0.f) {                      // uniform: softcap before ALiBi
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sc[e] = p.softcap * tanhf(sc[e] / p.softcap);
+        }
+        if (p.alibi) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sc[e] += slope * static_cast<float>(cell0 + (e >> 2) * 16 + (e & 3) - pos);
+        }
+        // tile max over visible scores (NaN left out; it is tracked per lane and
+        // merged over the lane groups at the end)
         bool vis[8];
         float tmax = kNegInf;
         bool tnan = false;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int kb = e >> 2, i = e & 3;
-            const int cell = lo + t0 + kb * 16 + 4 * lg + i;
-            const bool v = cell < lim;
-            float x = s[kb][i];
-            if constexpr (I8) x *= ksc_lds[kb * 16 + 4 * lg + i];
-            if (p.softcap > 0.f) x = p.softcap * tanhf(x / p.softcap);
-            x += slope * static_cast<float>(cell - pos);
-            vis[e] = v;
-            sc[e] = x;
-            if (v) {
-                if (x != x) tnan = true;
-                else tmax = max_keep(tmax, x);
-            }
-            if (p.dbg_visit && v) {
-                dbg_cnt += 1;
-                dbg_sum += cell;
-                dbg_sq += static_cast<long long>(cell) * cell;
-            }
+            vis[e] = (e >> 2) * 16 + (e & 3) < vlim;
+            tnan = tnan || (vis[e] && sc[e] != sc[e]);
+            tmax = fmaxf(tmax, vis[e] ? sc[e] : kNegInf);
         }
-        tmax = max_keep(tmax, wave_xor(tmax, 16));
-        tmax = max_keep(tmax, wave_xor(tmax, 32));
-        int tn = tnan ? 1 : 0;
-        tn |= wave_xor_i(tn, 16);
-        tn |= wave_xor_i(tn, 32);
-        nan_run = nan_run || tn;
-        m_true = max_keep(m_true, tmax);
+        nan_run = nan_run || tnan;
+        if (p.dbg_visit) {
+            unsigned long long c = 0, sm = 0, sq = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (vis[e]) {
+                    const unsigned long long cell = cell0 + (e >> 2) * 16 + (e & 3);
+                    c += 1;
+                    sm += cell;
+                    sq += cell * cell;
+                }
+            }
+            atomicAdd(my_dbg + 0, c);
+            atomicAdd(my_dbg + 1, sm);
+            atomicAdd(my_dbg + 2, sq);
+        }
+        tmax = fmaxf(tmax, wave_xor(tmax, 16));
+        tmax = fmaxf(tmax, wave_xor(tmax, 32));
+        m_true = fmaxf(m_true, tmax);
         const bool need = (tmax > m_use + kLazy) || (m_use == kNegInf && tmax != kNegInf);
         if (wave_any(need)) {
             const float c = need ? rescale_factor(m_use, tmax) : 1.f;
@@ -293,38 +345,59 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o_acc[db] *= c;
         }
+        // weights exp(s - m_use) (v_exp_f32; results below 2^-126 flush to zero)
+        const float mls = m_use * kLog2e;
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float w = vis[e] ? exp_diff(sc[e], m_use) : 0.f;
+            const float w = vis[e] ? __builtin_amdgcn_exp2f(fmaf(sc[e], kLog2e, -mls)) : 0.f;
             l_run += w;
             pv[e] = w;
-            if constexpr (I8) pv[e] *= vsc_lds[(e >> 2) * 16 + 4 * lg + (e & 3)];
+        }
+        if constexpr (I8) {
+            const float4 v0 = *reinterpret_cast<const float4*>(vsc_lds + 4 * lg);
+            const float4 v1 = *reinterpret_cast<const float4*>(vsc_lds + 16 + 4 * lg);
+            pv[0] *= v0.x; pv[1] *= v0.y; pv[2] *= v0.z; pv[3] *= v0.w;
+            pv[4] *= v1.x; pv[5] *= v1.y; pv[6] *= v1.z; pv[7] *= v1.w;
         }
         const u32x4 pop = u32x4{pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]),
                                 pack2<F16>(pv[4], pv[5]), pack2<F16>(pv[6], pv[7])};
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(vt_lds + vt_off(db * 16 + ln, lg));
+            const u32x4 a = *reinterpret_cast<const u32x4*>(vt_lds + vread[db & 1] + db * 1024);
             o_acc[db] = mfma16x16x32<F16>(a, pop, o_acc[db]);
         }
     };
 
-    // two register sets: the loads of tile t + 2 are in flight during tiles t and t + 1
-    Regs ra, rb;
-    if (n_keys > 0) load_tile(ra, 0);
-    if (n_keys > kTK) load_tile(rb, kTK);
-    for (int t0 = 0; t0 < n_keys; t0 += 2 * kTK) {
-        store_tile(ra);
-        __syncthreads();
-        if (t0 + 2 * kTK < n_keys) load_tile(ra, t0 + 2 * kTK);
-        if (wave_live) tile_math(t0);
-        __syncthreads();
-        if (t0 + kTK < n_keys) {
-            store_tile(rb);
+    if constexpr (W < 12) {
+        // two register sets: the loads of tile t + 2 are in flight during tiles t and t + 1
+        Regs ra, rb;
+        if (n_keys > 0) load_tile(ra, 0);
+        if (n_keys > kTK) load_tile(rb, kTK);
+        for (int t0 = 0; t0 < n_keys; t0 += 2 * kTK) {
+            store_tile(ra);
             __syncthreads();
-            if (t0 + 3 * kTK < n_keys) load_tile(rb, t0 + 3 * kTK);
-            if (wave_live) tile_math(t0 + kTK);
+            if (t0 + 2 * kTK < n_keys) load_tile(ra, t0 + 2 * kTK);
+            if (wave_live) tile_math(t0);
+            __syncthreads();
+            if (t0 + kTK < n_keys) {
+                store_tile(rb);
+                __syncthreads();
+                if (t0 + 3 * kTK < n_keys) load_tile(rb, t0 + 3 * kTK);
+                if (wave_live) tile_math(t0 + kTK);
+                __syncthreads();
+            }
+        }
+    } else {
+        // 12 waves share a SIMD three at a time (168 registers each): one set, the
+        // loads of tile t + 1 are in flight during tile t
+        Regs ra;
+        if (n_keys > 0) load_tile(ra, 0);
+        for (int t0 = 0; t0 < n_keys; t0 += kTK) {
+            store_tile(ra);
+            __syncthreads();
+            if (t0 + kTK < n_keys) load_tile(ra, t0 + kTK);
+            if (wave_live) tile_math(t0);
             __syncthreads();
         }
     }
@@ -334,23 +407,11 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     float l = l_run;
     l += wave_xor(l, 16);
     l += wave_xor(l, 32);
-    long long cnt = 0, sum = 0, sq = 0;
-    if (p.dbg_visit) {
-        auto xsum = [&](long long v) -> long long {
-            long long acc = v;
-            for (int msk = 16; msk <= 32; msk <<= 1) {
-                const unsigned lo32 = static_cast<unsigned>(acc & 0xffffffffLL);
-                const int hi32 = static_cast<int>(acc >> 32);
-                const unsigned olo = static_cast<unsigned>(wave_xor_i(static_cast<int>(lo32), msk));
-                const int ohi = wave_xor_i(hi32, msk);
-                acc += static_cast<long long>(
-                    (static_cast<unsigned long long>(static_cast<unsigned>(ohi)) << 32) | olo);
-            }
-            return acc;
-        };
-        cnt = xsum(dbg_cnt);
-        sum = xsum(dbg_sum);
-        sq = xsum(dbg_sq);
+    {
+        int tn = nan_run ? 1 : 0;
+        tn |= wave_xor_i(tn, 16);
+        tn |= wave_xor_i(tn, 32);
+        nan_run = tn != 0;
     }
     if (!ok) return;
     const bool bad = nan_run || m_true == kPosInf;
@@ -373,9 +434,9 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     }
     if (p.dbg_visit && lg == 0 && m % G == 0) {
         const int64_t di = ((static_cast<int64_t>(b) * p.R + r) * p.Hkv + g) * p.n_slices_max + t_split;
-        p.dbg_visit[di * 3 + 0] = cnt;
-        p.dbg_visit[di * 3 + 1] = sum;
-        p.dbg_visit[di * 3 + 2] = sq;
+        p.dbg_visit[di * 3 + 0] = static_cast<int64_t>(my_dbg[0]);
+        p.dbg_visit[di * 3 + 1] = static_cast<int64_t>(my_dbg[1]);
+        p.dbg_visit[di * 3 + 2] = static_cast<int64_t>(my_dbg[2]);
     }
 }
 

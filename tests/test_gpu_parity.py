@@ -184,6 +184,34 @@ def test_decode_empty_rows_are_zero():
     assert np.all(out[1, :2] == 0)
 
 
+@pytest.mark.parametrize("kind", ["one_block_bf16", "work_group_bf16", "work_group_i8"])
+def test_decode_nan_propagation(kind):
+    """A NaN key element (or int8 key scale) makes exactly the query vectors that
+    see that key NaN; causal rows that cannot see it stay finite."""
+    shapes = {"one_block_bf16": dict(n_row=1, n_head_q=8, kv_dtype="bf16"),
+              "work_group_bf16": dict(n_row=6, n_head_q=16, kv_dtype="bf16"),
+              "work_group_i8": dict(n_row=6, n_head_q=24, kv_dtype="i8")}[kind]
+    wl = gen.make_decode(seed=[12, len(kind)], n_stream=2, n_head_kv=2, head_dim=128, cap=700,
+                         depths=[700, 500], slice_len=256, **shapes)
+    R, G = wl.n_row, wl.n_head_q // wl.n_head_kv
+    k = wl.k.copy()
+    ks = None if wl.k_scale is None else wl.k_scale.copy()
+    for b, cell, g in [(0, 300, 1), (1, 497, 0)]:
+        if ks is not None:
+            ks[b, cell, g] = np.nan
+        else:
+            k[b, cell, g, 5] = 0x7FC0
+    wl.k, wl.k_scale = k, ks
+    out = hip_run.run_decode(wl)
+    nmse_check(out, oracle_decode(wl), TOL[wl.kv_dtype], kind)
+    assert np.isnan(out[0, :, G:2 * G]).all() and np.isfinite(out[0, :, :G]).all()
+    # stream 1: row r sits at 500 - R + r and sees cell 497 iff 497 <= 500 - R + r
+    for r in range(R):
+        sees = 497 <= 500 - R + r
+        assert np.isnan(out[1, r, :G]).all() == sees and np.isfinite(out[1, r, :G]).all() != sees
+        assert np.isfinite(out[1, r, G:]).all()
+
+
 # ----------------------------------------------------------------------------
 # prefill
 # ----------------------------------------------------------------------------
