@@ -111,10 +111,15 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     const float slope = (p.alibi && ok) ? p.alibi[h] : 0.f;
 
     // keys no query vector of the work-group can see are never loaded
-    int lim_max = -1;
-    for (int rr = m_wg / G; rr <= (m_end - 1) / G && rr < p.R; ++rr)
-        lim_max = max(lim_max, p.causal ? min(kvl - p.R + rr + 1, kvl) : kvl);
+    // (lim_max); keys below lim_min are seen by every query vector of it
+    int lim_max = -1, lim_min = 0x7fffffff;
+    for (int rr = m_wg / G; rr <= (m_end - 1) / G && rr < p.R; ++rr) {
+        const int l = p.causal ? min(kvl - p.R + rr + 1, kvl) : kvl;
+        lim_max = max(lim_max, l);
+        lim_min = min(lim_min, l);
+    }
     const int n_keys = max(0, min(hi, lim_max) - lo);
+    const int n_full = max(0, min(hi, lim_min) - lo);      // key slots visible to all
 
     // ---- tile loads ----------------------------------------------------------
     // Buffer loads through a descriptor that starts at the unit's first key row and
@@ -183,10 +188,10 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                     u32x4 w0, w1;
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        w0[2 * j] = i8_to_bf16(rw[j], 0) | (i8_to_bf16(rw[j], 1) << 16);
-                        w0[2 * j + 1] = i8_to_bf16(rw[j], 2) | (i8_to_bf16(rw[j], 3) << 16);
-                        w1[2 * j] = i8_to_bf16(rw[2 + j], 0) | (i8_to_bf16(rw[2 + j], 1) << 16);
-                        w1[2 * j + 1] = i8_to_bf16(rw[2 + j], 2) | (i8_to_bf16(rw[2 + j], 3) << 16);
+                        w0[2 * j] = i8pair_bf16(rw[j], 0, rw[j], 1);
+                        w0[2 * j + 1] = i8pair_bf16(rw[j], 2, rw[j], 3);
+                        w1[2 * j] = i8pair_bf16(rw[2 + j], 0, rw[2 + j], 1);
+                        w1[2 * j + 1] = i8pair_bf16(rw[2 + j], 2, rw[2 + j], 3);
                     }
                     *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch, D)) = w0;
                     *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch + 1, D)) = w1;
@@ -216,8 +221,8 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                         const int wbc = (hc * 8 + 4 * h + c) * 64 + ((gq ^ ((2 * hc + h) & 3)) << 4) + 8 * kb;
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj) {
-                            const uint32_t lo2 = i8_to_bf16(w[0][h], jj) | (i8_to_bf16(w[1][h], jj) << 16);
-                            const uint32_t hi2 = i8_to_bf16(w[2][h], jj) | (i8_to_bf16(w[3][h], jj) << 16);
+                            const uint32_t lo2 = i8pair_bf16(w[0][h], jj, w[1][h], jj);
+                            const uint32_t hi2 = i8pair_bf16(w[2][h], jj, w[3][h], jj);
                             *reinterpret_cast<uint2*>(vt_lds + (wbc ^ (jj << 6))) = uint2{lo2, hi2};
                         }
                     }
@@ -288,7 +293,6 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         }
         // score e of this lane is key cell0 + off(e): off = (e >> 2) * 16 + (e & 3)
         const int cell0 = lo + t0 + 4 * lg;
-        const int vlim = lim - cell0;               // visible iff off(e) < vlim
         float sc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) sc[e] = s[e >> 2][e & 3];
@@ -307,23 +311,25 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
             for (int e = 0; e < 8; ++e)
                 sc[e] += slope * static_cast<float>(cell0 + (e >> 2) * 16 + (e & 3) - pos);
         }
-        // tile max over visible scores (NaN left out; it is tracked per lane and
-        // merged over the lane groups at the end)
-        bool vis[8];
+        // Visibility: a tile whose keys every query vector of the work-group sees
+        // (uniform test) skips the per-score masks.  A NaN score is left out of the
+        // maximum (v_max_f32 returns the other operand) and shows up as a NaN weight,
+        // hence a NaN running sum, which the epilogue turns into the NaN flag.
+        const bool full = t0 + kTK <= n_full;
+        const int vlim = lim - cell0;               // partial tile: visible iff off(e) < vlim
         float tmax = kNegInf;
-        bool tnan = false;
+        if (full) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            vis[e] = (e >> 2) * 16 + (e & 3) < vlim;
-            tnan = tnan || (vis[e] && sc[e] != sc[e]);
-            tmax = fmaxf(tmax, vis[e] ? sc[e] : kNegInf);
+            for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, sc[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, (e >> 2) * 16 + (e & 3) < vlim ? sc[e] : kNegInf);
         }
-        nan_run = nan_run || tnan;
         if (p.dbg_visit) {
             unsigned long long c = 0, sm = 0, sq = 0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                if (vis[e]) {
+                if (full || (e >> 2) * 16 + (e & 3) < vlim) {
                     const unsigned long long cell = cell0 + (e >> 2) * 16 + (e & 3);
                     c += 1;
                     sm += cell;
@@ -348,12 +354,16 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         // weights exp(s - m_use) (v_exp_f32; results below 2^-126 flush to zero)
         const float mls = m_use * kLog2e;
         float pv[8];
+        if (full) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float w = vis[e] ? __builtin_amdgcn_exp2f(fmaf(sc[e], kLog2e, -mls)) : 0.f;
-            l_run += w;
-            pv[e] = w;
+            for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], kLog2e, -mls));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pv[e] = (e >> 2) * 16 + (e & 3) < vlim ? __builtin_amdgcn_exp2f(fmaf(sc[e], kLog2e, -mls)) : 0.f;
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) l_run += pv[e];
         if constexpr (I8) {
             const float4 v0 = *reinterpret_cast<const float4*>(vsc_lds + 4 * lg);
             const float4 v1 = *reinterpret_cast<const float4*>(vsc_lds + 16 + 4 * lg);
@@ -408,7 +418,8 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     l += wave_xor(l, 16);
     l += wave_xor(l, 32);
     {
-        int tn = nan_run ? 1 : 0;
+        // a NaN visible score made this lane's running sum NaN
+        int tn = (l_run != l_run) ? 1 : 0;
         tn |= wave_xor_i(tn, 16);
         tn |= wave_xor_i(tn, 32);
         nan_run = tn != 0;

@@ -271,10 +271,10 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                     u32x4 w0, w1;
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        w0[2 * j] = i8_to_bf16(rw[j], 0) | (i8_to_bf16(rw[j], 1) << 16);
-                        w0[2 * j + 1] = i8_to_bf16(rw[j], 2) | (i8_to_bf16(rw[j], 3) << 16);
-                        w1[2 * j] = i8_to_bf16(rw[2 + j], 0) | (i8_to_bf16(rw[2 + j], 1) << 16);
-                        w1[2 * j + 1] = i8_to_bf16(rw[2 + j], 2) | (i8_to_bf16(rw[2 + j], 3) << 16);
+                        w0[2 * j] = i8pair_bf16(rw[j], 0, rw[j], 1);
+                        w0[2 * j + 1] = i8pair_bf16(rw[j], 2, rw[j], 3);
+                        w1[2 * j] = i8pair_bf16(rw[2 + j], 0, rw[2 + j], 1);
+                        w1[2 * j + 1] = i8pair_bf16(rw[2 + j], 2, rw[2 + j], 3);
                     }
                     *reinterpret_cast<u32x4*>(k_lds + k16_off(key, 2 * ch, D)) = w0;
                     *reinterpret_cast<u32x4*>(k_lds + k16_off(key, 2 * ch + 1, D)) = w1;
@@ -293,8 +293,8 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                     uint32_t lo2, hi2;
                     if constexpr (I8) {
                         const int w = dd >> 2, by = dd & 3;
-                        lo2 = i8_to_bf16(vreg[i][0][w], by) | (i8_to_bf16(vreg[i][1][w], by) << 16);
-                        hi2 = i8_to_bf16(vreg[i][2][w], by) | (i8_to_bf16(vreg[i][3][w], by) << 16);
+                        lo2 = i8pair_bf16(vreg[i][0][w], by, vreg[i][1][w], by);
+                        hi2 = i8pair_bf16(vreg[i][2][w], by, vreg[i][3][w], by);
                     } else {
                         const int w = dd >> 1;
                         if (dd & 1) {

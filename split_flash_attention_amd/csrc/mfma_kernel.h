@@ -80,23 +80,27 @@ struct MParams {
 // ---------------------------------------------------------------------------
 // 16-bit conversions and LDS addressing
 // ---------------------------------------------------------------------------
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> packed 16-bit pair, round to nearest even (one v_cvt_pk_* each)
 template <bool F16>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    uint16_t a, b;
-    if constexpr (F16) {
-        a = __builtin_bit_cast(uint16_t, static_cast<_Float16>(lo));
-        b = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hi));
-    } else {
-        a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
-        b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
-    }
-    return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+    if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-// bf16 bits of int8 byte `byte` of `word` (exact: |x| <= 128 fits 8 significant bits)
-__device__ __forceinline__ uint32_t i8_to_bf16(uint32_t word, int byte) {
-    const float f = static_cast<float>(static_cast<int8_t>((word >> (8 * byte)) & 0xffu));
-    return __float_as_uint(f) >> 16;
+// int8 byte `byte` of `word` as a float (exact)
+__device__ __forceinline__ float i8_float(uint32_t word, int byte) {
+    return static_cast<float>(static_cast<int8_t>((word >> (8 * byte)) & 0xffu));
+}
+
+// bf16 pair {bytes (wa, ba), (wb, bb)} of int8 data: an int8 value fits 8
+// significant bits, so the high half of its float is its exact bf16; one
+// v_perm_b32 takes both high halves
+__device__ __forceinline__ uint32_t i8pair_bf16(uint32_t wa, int ba, uint32_t wb, int bb) {
+    return __builtin_amdgcn_perm(__float_as_uint(i8_float(wb, bb)), __float_as_uint(i8_float(wa, ba)), 0x07060302u);
 }
 
 // byte offset of 16-byte chunk `ch` (8 dims) of key row `key` in the K tile; chunks
@@ -361,10 +365,10 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                     u32x4 w0, w1;
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        w0[2 * j] = i8_to_bf16(r[j], 0) | (i8_to_bf16(r[j], 1) << 16);
-                        w0[2 * j + 1] = i8_to_bf16(r[j], 2) | (i8_to_bf16(r[j], 3) << 16);
-                        w1[2 * j] = i8_to_bf16(r[2 + j], 0) | (i8_to_bf16(r[2 + j], 1) << 16);
-                        w1[2 * j + 1] = i8_to_bf16(r[2 + j], 2) | (i8_to_bf16(r[2 + j], 3) << 16);
+                        w0[2 * j] = i8pair_bf16(r[j], 0, r[j], 1);
+                        w0[2 * j + 1] = i8pair_bf16(r[j], 2, r[j], 3);
+                        w1[2 * j] = i8pair_bf16(r[2 + j], 0, r[2 + j], 1);
+                        w1[2 * j + 1] = i8pair_bf16(r[2 + j], 2, r[2 + j], 3);
                     }
                     *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch, D)) = w0;
                     *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch + 1, D)) = w1;
@@ -384,8 +388,8 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                     uint32_t lo2, hi2;
                     if constexpr (I8) {
                         const int w = dd >> 2, by = dd & 3;
-                        lo2 = i8_to_bf16(vreg[i][0][w], by) | (i8_to_bf16(vreg[i][1][w], by) << 16);
-                        hi2 = i8_to_bf16(vreg[i][2][w], by) | (i8_to_bf16(vreg[i][3][w], by) << 16);
+                        lo2 = i8pair_bf16(vreg[i][0][w], by, vreg[i][1][w], by);
+                        hi2 = i8pair_bf16(vreg[i][2][w], by, vreg[i][3][w], by);
                     } else {
                         const int w = dd >> 1;
                         if (dd & 1) {
