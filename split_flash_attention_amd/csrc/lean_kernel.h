@@ -35,15 +35,17 @@ __device__ __forceinline__ int vt16_off(int d, int slot) {
     return pr * 32 + ((slot ^ (((pr >> 3) & 1) << 1)) << 3);
 }
 
+// LDS: K tile, V^T tile, the tile's int8 scales, the cells of the next two tiles
+// (selection mode), the visit counters, then the selection list.
 template <int D>
 constexpr int lean_base_smem() {
-    return kLT * D * 2 + D * 32 + 2 * kLT * 4;
+    return kLT * D * 2 + D * 32 + 2 * kLT * 4 + 2 * kLT * 4 + 16 * 3 * 8;
 }
 
 // CP: cache policy of the decode K/V stream loads (0 default, 2 non-temporal).
 template <int MODE, int KT, int D, int CP>
 __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, const int gy, const int bz,
-                                          char* smem, int& s_nids) {
+                                          char* smem) {
     constexpr bool F16 = (KT == SEL_ATTN_F16);
     constexpr bool I8 = (KT == SEL_ATTN_I8);
     constexpr int NKK = D / 32;
@@ -59,7 +61,9 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     char* vt_lds = smem + kLT * D * 2;
     float* ksc_lds = reinterpret_cast<float*>(vt_lds + D * 32);
     float* vsc_lds = ksc_lds + kLT;
-    int* list = reinterpret_cast<int*>(vsc_lds + kLT);
+    int* tcell = reinterpret_cast<int*>(vsc_lds + kLT);                       // [2][kLT]
+    unsigned long long* dbg_lds = reinterpret_cast<unsigned long long*>(tcell + 2 * kLT);   // [16][3]
+    int* list = reinterpret_cast<int*>(dbg_lds + 16 * 3);
 
     const int lane = threadIdx.x;
     const int ln = lane & 15;
@@ -93,7 +97,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     int pos, lim;
     if constexpr (MODE == kDecode) {
         pos = kvl - p.R + r;
-        lim = p.causal ? min(pos + 1, kvl) : kvl;
+        lim = min(p.causal ? min(pos + 1, kvl) : kvl, hi);
     } else {
         pos = p.q_pos ? p.q_pos[r] : 0;
         lim = 0x7fffffff;
@@ -125,8 +129,10 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     const float slope = (p.alibi && ok) ? p.alibi[h] : 0.f;
 
     // ---- key slots --------------------------------------------------------------
-    int n_keys;
+    int n_keys, n_full = 0;
     if constexpr (MODE == kSel) {
+        // the row's list: invalid ids become +inf, bitonic sort in LDS, then the
+        // repeats are dropped by a wave-wide compaction (ballot + prefix count)
         const int P = p.sel_pow2;
         const int32_t* srow = p.sel + static_cast<int64_t>(row0) * p.n_sel;
         for (int e = lane; e < P; e += 64) {
@@ -150,18 +156,24 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                 __syncthreads();
             }
         }
-        if (lane == 0) {
-            int w = 0, prev = -1;
-            for (int e = 0; e < P; ++e) {
-                const int x = list[e];
-                if (x == 0x7fffffff) break;
-                if (x != prev) list[w++] = x;
-                prev = x;
-            }
-            s_nids = w;
+        // keep element e if it is valid and differs from element e - 1; kept
+        // elements move down to their rank (never above their own index, and each
+        // block is read before it is written, so in place is safe)
+        int n_ids = 0, prev = -1;
+        for (int base = 0; base < P; base += 64) {
+            const int e = base + lane;
+            const int x = e < P ? list[e] : 0x7fffffff;
+            const int up = __shfl_up(x, 1, 64);          // every lane takes part in the exchange
+            const int before = lane > 0 ? up : prev;
+            const bool keep = x != 0x7fffffff && x != before;
+            const unsigned long long bal = __ballot(keep);
+            const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+            prev = __shfl(x, 63, 64);
+            __syncthreads();
+            if (keep) list[n_ids + rank] = x;
+            n_ids += __popcll(bal);
+            __syncthreads();
         }
-        __syncthreads();
-        const int n_ids = s_nids;
         if (p.dbg_sel && t_split == 0 && qchunk == 0) {
             int32_t* dst = p.dbg_sel + (static_cast<int64_t>(row0) * p.Hkv + g) * (1 + p.n_sel);
             if (lane == 0) dst[0] = n_ids;
@@ -169,20 +181,31 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         }
         n_keys = n_ids * p.bs;
     } else {
-        int lim_max = -1;
+        int lim_max = -1, lim_min = 0x7fffffff;
         const int m_end = min(p.M, m_wg + 16);
-        for (int rr = m_wg / G; rr <= (m_end - 1) / G && rr < p.R; ++rr)
-            lim_max = max(lim_max, p.causal ? min(kvl - p.R + rr + 1, kvl) : kvl);
+        for (int rr = m_wg / G; rr <= (m_end - 1) / G && rr < p.R; ++rr) {
+            const int l = p.causal ? min(kvl - p.R + rr + 1, kvl) : kvl;
+            lim_max = max(lim_max, l);
+            lim_min = min(lim_min, l);
+        }
         n_keys = max(0, min(hi, lim_max) - lo);
+        n_full = max(0, min(hi, lim_min) - lo);        // slots every query vector sees
     }
 
-    auto slot_cell = [&](int kslot) -> int {
-        if (kslot >= n_keys) return -1;
+    // Selection mode: the cells of a tile's 16 slots are looked up once, by lanes
+    // 0..15, into tcell[tile & 1] (-1 for none), a tile ahead of their use.
+    auto fill_cells = [&](int t0) {
         if constexpr (MODE == kSel) {
-            const int c = list[kslot / p.bs] * p.bs + kslot % p.bs;
-            return (c < p.n_kv && c >= lo && c < hi) ? c : -1;
-        } else {
-            return lo + kslot;
+            if (lane < kLT) {
+                const int kslot = t0 + lane;
+                int c = -1;
+                if (kslot < n_keys) {
+                    const int id = list[kslot / p.bs];
+                    const int cc = id * p.bs + kslot % p.bs;
+                    if (cc < p.n_kv && cc >= lo && cc < hi) c = cc;
+                }
+                tcell[((t0 / kLT) & 1) * kLT + lane] = c;
+            }
         }
     };
 
@@ -223,11 +246,12 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     u32x4 vreg[NVL][4];
     float kscr = 0.f, vscr = 0.f;
     auto load_tile = [&](int t0) {
+        const int* tc = tcell + ((t0 / kLT) & 1) * kLT;
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
             const int e = lane + 64 * i;
             if constexpr (MODE == kSel) {
-                const int cell = e < K_TASKS ? slot_cell(t0 + e / GCH) : -1;
+                const int cell = e < K_TASKS ? tc[e / GCH] : -1;
                 const int off = cell >= 0 ? cell * cb + (e % GCH) * 16 : kAbsent;
                 kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
             } else {
@@ -242,7 +266,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if constexpr (MODE == kSel) {
-                    const int cell = e < V_TASKS ? slot_cell(t0 + 4 * (e & 3) + j) : -1;
+                    const int cell = e < V_TASKS ? tc[4 * (e & 3) + j] : -1;
                     const int off = cell >= 0 ? cell * cb + (e >> 2) * 16 : kAbsent;
                     vreg[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
                 } else {
@@ -254,7 +278,9 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         }
         if constexpr (I8) {
             if (lane < kLT) {
-                const int cell = slot_cell(t0 + lane);
+                int cell;
+                if constexpr (MODE == kSel) cell = tc[lane];
+                else cell = t0 + lane < n_keys ? lo + t0 + lane : -1;
                 kscr = cell >= 0 ? p.ksc[sc_base + cell * p.sc_sc] : 0.f;
                 vscr = cell >= 0 ? p.vsc[sc_base + cell * p.sc_sc] : 0.f;
             }
@@ -319,55 +345,96 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
 
     // ---- running state ---------------------------------------------------------
     float m_use = kNegInf;     // exponent reference of o and l
-    float m_true = kNegInf;    // largest finite-or-infinite visible score seen
+    float m_true = kNegInf;    // largest visible non-NaN score seen
     float l_run = 0.f;
-    bool nan_run = false;
-    long long dbg_cnt = 0, dbg_sum = 0, dbg_sq = 0;
     f32x4 o_acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // visit counters of this lane's query vector in LDS (no registers in the loop)
+    unsigned long long* my_dbg = dbg_lds + ln * 3;
+    if (p.dbg_visit && lg == 0) my_dbg[0] = my_dbg[1] = my_dbg[2] = 0ull;
 
-    if (n_keys > 0) load_tile(0);
+    // Operand read addresses as base + immediate offset.  K (k16_off): row ln, chunk
+    // kk * 4 + lg XOR-ed with ln, which only touches the low two bits of kk: four
+    // bases.  V^T (vt16_off): dim db * 16 + ln, whose row XOR (2 * db + (ln >> 3)) & 7
+    // repeats with db & 3 and whose slot XOR does not depend on db: four bases.
+    int kread[4], vread[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        kread[q] = ln * D * 2 + (((q * 4 + lg) ^ ln) << 4);
+        vread[q] = (ln ^ ((2 * q + (ln >> 3)) & 7)) * 32 + ((lg ^ (((ln >> 3) & 1) << 1)) << 3);
+    }
+
+    if (n_keys > 0) {
+        fill_cells(0);
+        __syncthreads();                        // tcell written by lanes 0..15, read by all
+        load_tile(0);
+    }
     for (int t0 = 0; t0 < n_keys; t0 += kLT) {
         store_tile();
+        if (t0 + kLT < n_keys) fill_cells(t0 + kLT);
         __syncthreads();
         if (t0 + kLT < n_keys) load_tile(t0 + kLT);
 
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(k_lds + k16_off(ln, kk * 4 + lg, D));
+            const u32x4 a = *reinterpret_cast<const u32x4*>(k_lds + kread[kk & 3] + (kk >> 2) * 256);
             s = mfma16x16x32<F16>(a, qop[kk], s);
         }
 
-        float sc[4];
-        bool vis[4];
-        int cell_of[4];
-        float tmax = kNegInf;
-        bool tnan = false;
+        // scores of keys 4 * lg + i of the tile: scale (int8 key scale), softcap,
+        // ALiBi; visibility; tile maximum.  A NaN score is left out of the maximum
+        // (v_max_f32 returns the other operand) and shows up as a NaN weight, hence
+        // a NaN running sum, which the epilogue turns into the NaN flag.
+        int cell[4];
+        bool full;
+        if constexpr (MODE == kSel) {
+            const int4 c4 = *reinterpret_cast<const int4*>(tcell + ((t0 / kLT) & 1) * kLT + 4 * lg);
+            cell[0] = c4.x; cell[1] = c4.y; cell[2] = c4.z; cell[3] = c4.w;
+            full = false;
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int cell = slot_cell(t0 + 4 * lg + i);
-            cell_of[i] = cell;
-            const bool v = cell >= 0 && cell < lim;
-            float x = s[i];
-            if constexpr (I8) x *= ksc_lds[4 * lg + i];
-            if (p.softcap > 0.f) x = p.softcap * tanhf(x / p.softcap);
-            x += slope * static_cast<float>(cell - pos);
-            vis[i] = v;
-            sc[i] = x;
-            if (v) {
-                if (x != x) tnan = true;
-                else tmax = max_keep(tmax, x);
-            }
+            for (int i = 0; i < 4; ++i) cell[i] = lo + t0 + 4 * lg + i;
+            full = t0 + kLT <= n_full;                 // uniform: every query vector sees the tile
         }
-        tmax = max_keep(tmax, wave_xor(tmax, 16));
-        tmax = max_keep(tmax, wave_xor(tmax, 32));
-        int tn = tnan ? 1 : 0;
-        tn |= wave_xor_i(tn, 16);
-        tn |= wave_xor_i(tn, 32);
-        nan_run = nan_run || tn;
-        m_true = max_keep(m_true, tmax);
+        bool vis[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vis[i] = full || (cell[i] >= 0 && cell[i] < lim);
+        float sc[4] = {s[0], s[1], s[2], s[3]};
+        if constexpr (I8) {
+            const float4 k4 = *reinterpret_cast<const float4*>(ksc_lds + 4 * lg);
+            sc[0] *= k4.x; sc[1] *= k4.y; sc[2] *= k4.z; sc[3] *= k4.w;
+        }
+        if (p.softcap > 0.f) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i] = p.softcap * tanhf(sc[i] / p.softcap);
+        }
+        if (p.alibi) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i] += slope * static_cast<float>(cell[i] - pos);
+        }
+        float tmax = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, vis[i] ? sc[i] : kNegInf);
+        if (p.dbg_visit) {
+            unsigned long long c = 0, sm = 0, sq = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (vis[i]) {
+                    const unsigned long long ce = static_cast<unsigned long long>(cell[i]);
+                    c += 1;
+                    sm += ce;
+                    sq += ce * ce;
+                }
+            }
+            atomicAdd(my_dbg + 0, c);
+            atomicAdd(my_dbg + 1, sm);
+            atomicAdd(my_dbg + 2, sq);
+        }
+        tmax = fmaxf(tmax, wave_xor(tmax, 16));
+        tmax = fmaxf(tmax, wave_xor(tmax, 32));
+        m_true = fmaxf(m_true, tmax);
         const bool need = (tmax > m_use + kLazy) || (m_use == kNegInf && tmax != kNegInf);
         if (wave_any(need)) {
             const float c = need ? rescale_factor(m_use, tmax) : 1.f;
@@ -376,27 +443,22 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o_acc[db] *= c;
         }
+        // weights exp(s - m_use) (v_exp_f32; results below 2^-126 flush to zero)
+        const float mls = m_use * kLog2e;
         float pe[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pe[i] = vis[i] ? exp_diff(sc[i], m_use) : 0.f;
+            pe[i] = vis[i] ? __builtin_amdgcn_exp2f(fmaf(sc[i], kLog2e, -mls)) : 0.f;
             l_run += pe[i];
-            if constexpr (I8) pe[i] *= vsc_lds[4 * lg + i];
+        }
+        if constexpr (I8) {
+            const float4 v4 = *reinterpret_cast<const float4*>(vsc_lds + 4 * lg);
+            pe[0] *= v4.x; pe[1] *= v4.y; pe[2] *= v4.z; pe[3] *= v4.w;
         }
         const u32x2 pop = u32x2{pack2<F16>(pe[0], pe[1]), pack2<F16>(pe[2], pe[3])};
-        if (p.dbg_visit) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (vis[i]) {
-                    dbg_cnt += 1;
-                    dbg_sum += cell_of[i];
-                    dbg_sq += static_cast<long long>(cell_of[i]) * cell_of[i];
-                }
-            }
-        }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const u32x2 a = *reinterpret_cast<const u32x2*>(vt_lds + vt16_off(db * 16 + ln, lg));
+            const u32x2 a = *reinterpret_cast<const u32x2*>(vt_lds + vread[db & 3] + db * 512);
             o_acc[db] = mfma16x16x16<F16>(a, pop, o_acc[db]);
         }
         __syncthreads();
@@ -406,24 +468,10 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     float l = l_run;
     l += wave_xor(l, 16);
     l += wave_xor(l, 32);
-    long long cnt = 0, sum = 0, sq = 0;
-    if (p.dbg_visit) {
-        auto xsum = [&](long long v) -> long long {
-            long long acc = v;
-            for (int msk = 16; msk <= 32; msk <<= 1) {
-                const unsigned lo32 = static_cast<unsigned>(acc & 0xffffffffLL);
-                const int hi32 = static_cast<int>(acc >> 32);
-                const unsigned olo = static_cast<unsigned>(wave_xor_i(static_cast<int>(lo32), msk));
-                const int ohi = wave_xor_i(hi32, msk);
-                acc += static_cast<long long>(
-                    (static_cast<unsigned long long>(static_cast<unsigned>(ohi)) << 32) | olo);
-            }
-            return acc;
-        };
-        cnt = xsum(dbg_cnt);
-        sum = xsum(dbg_sum);
-        sq = xsum(dbg_sq);
-    }
+    int tn = (l_run != l_run) ? 1 : 0;           // a NaN visible score made a running sum NaN
+    tn |= wave_xor_i(tn, 16);
+    tn |= wave_xor_i(tn, 32);
+    const bool nan_run = tn != 0;
     if (!ok) return;
     const bool bad = nan_run || m_true == kPosInf;
     const bool empty = !bad && m_true == kNegInf;
@@ -463,23 +511,22 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
             di = ((static_cast<int64_t>(b) * p.R + r) * p.Hkv + g) * p.n_slices_max + t_split;
         else
             di = (static_cast<int64_t>(r) * p.Hkv + g) * p.n_splits + t_split;
-        p.dbg_visit[di * 3 + 0] = cnt;
-        p.dbg_visit[di * 3 + 1] = sum;
-        p.dbg_visit[di * 3 + 2] = sq;
+        p.dbg_visit[di * 3 + 0] = static_cast<int64_t>(my_dbg[0]);
+        p.dbg_visit[di * 3 + 1] = static_cast<int64_t>(my_dbg[1]);
+        p.dbg_visit[di * 3 + 2] = static_cast<int64_t>(my_dbg[2]);
     }
 }
 
 template <int MODE, int KT, int D, int CP>
 __global__ __launch_bounds__(64, 2) void lean_attn_kernel(MParams p) {
     extern __shared__ __align__(16) char smem[];
-    __shared__ int s_nids;
     if constexpr (MODE == kDecode) {
         for_each_decode_item(p, [&](int t, int gy, int bz) {
-            lean_unit<MODE, KT, D, CP>(p, t, gy, bz, smem, s_nids);
+            lean_unit<MODE, KT, D, CP>(p, t, gy, bz, smem);
             __syncthreads();
         });
     } else {
-        lean_unit<MODE, KT, D, CP>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem, s_nids);
+        lean_unit<MODE, KT, D, CP>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem);
     }
 }
 
