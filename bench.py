@@ -33,21 +33,25 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
 # HBM bytes of one decode launch on the split-K workload, from two rocprofv3 --pmc
 # runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
-# by what the same counter reads for the 1 GiB device copy.  The figures describe
-# the kernel sources they were taken on (SHA-256 below); once those change they
-# are stale and `traffic` is reported as null.
-DECODE_TRAFFIC = None
+# by what the same counter reads for the 1 GiB device copy (FETCH_SIZE reads half
+# the copied bytes: factor 2.0; WRITE_SIZE reads them all: factor 1.0).  The
+# figures describe the decode kernel's sources as they were when measured (the
+# SHA-256 below); once those change they are stale and `traffic` is null.
+DECODE_TRAFFIC = {"sources_sha256": "397dd4e69987c802abf06a5e890aa9c76bd5575bd23ec34031f3d6d41a483dc4",
+                  "fetch_bytes": 592918.1875 * 1024 * 2.0,
+                  "write_bytes": 10595.0625 * 1024 * 1.0}
+# the files the decode kernel is built from
+DECODE_SOURCES = ["arch.h", "common.h", "internal.h", "mfma_kernel.h", "lean_kernel.h", "mfma_decode.hip"]
 
 
 def kernel_sources_sha256():
-    """SHA-256 over the HIP sources of the library (file names and contents, sorted)."""
+    """SHA-256 over the decode kernel's source files (names and contents, in order)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "split_flash_attention_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".h", ".hip")):
-            h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
+    for f in DECODE_SOURCES:
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
@@ -106,12 +110,13 @@ def cpu_baseline_decode(wl, min_seconds=12.0):
                       causal=wl.causal, scale=wl.scale)
         cells += int(wl.kv_len[b])
         n_calls += 1
+    # (the whole workload takes about 1.4 s on 16 cores, so the sample repeats it)
     dt = time.perf_counter() - t0
     nbytes = cells * wl.n_head_kv * wl.head_dim * 2 * 2
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"split-K decode workload, its first {n_calls} streams in order (cycling), "
-                      f"{cells} cells x 32 heads, {dt:.1f} s"}
+            "sample": f"split-K decode workload: {n_calls} single-stream passes over its 16 streams "
+                      f"in order, {cells} cells x 32 query heads, {dt:.1f} s"}
 
 
 def main():
