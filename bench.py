@@ -11,7 +11,9 @@ rate in GB/s (algorithmic bytes: every visible K and V row read once).
 The same run also times the maskless selected-key prefill (2048 rows at
 positions 30000..32047, 16/2 heads, head dim 256, bf16, 512 block ids per row
 over 4-cell blocks) and reports its TFLOP/s (4*D flops per visited (row, head,
-key)), and a plain device copy of 1 GiB (the achievable copy rate, and the
+key)), the selected-key decode (16 rows, one per sequence of a unified cache, with
+the same lists and block size, the key range split 32 ways, then the combine),
+and a plain device copy of 1 GiB (the achievable copy rate, and the
 calibration for the memory counters).  `--verify` adds the int8 verify-window
 decode (16 streams x 16 rows, 48/4 heads, depth 32000, slices of 2048).
 
@@ -29,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+SEL_DECODE_SPLITS = 32         # key-range splits of the selected-key decode rows (16 rows x 2 kv heads each)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
 # HBM bytes of one decode launch on the split-K workload, from two rocprofv3 --pmc
@@ -145,6 +148,11 @@ def main():
     wl3 = gen.config3()
     d3 = hip_run.PrefillDev(wl3, "cuda", poison_outputs=False)
     a3 = d3.args()
+    log("generating the selected-key decode workload")
+    wl6 = gen.sel_decode()
+    d6 = hip_run.PrefillDev(wl6, "cuda", n_splits=SEL_DECODE_SPLITS, poison_outputs=False)
+    a6 = d6.args()
+    c6 = sa.combine_args(part_o=d6.part_o, part_ml=d6.part_ml, out=d6.out.view(1, *d6.out.shape))
     copy_src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")     # 1 GiB
     copy_dst = torch.empty_like(copy_src)
     copy_src.fill_(1.0)
@@ -162,10 +170,15 @@ def main():
     def copy():
         copy_dst.copy_(copy_src)
 
+    def sel_decode():
+        sa.sel_attn_prefill(a6)
+        sa.sel_attn_split_combine(c6)
+
     log("warmup")
     for _ in range(args.warmup):
         step()
         prefill()
+        sel_decode()
         copy()
     torch.cuda.synchronize()
 
@@ -175,6 +188,7 @@ def main():
     ms_decode = timed(decode_only, args.steps, torch)
     ms_prefill = timed(prefill, args.steps, torch)
     ms_copy = timed(copy, max(3, args.steps // 4), torch)
+    ms_sd = timed(sel_decode, args.steps, torch)
 
     cells = int(np.asarray(wl2.kv_len, np.int64).sum())
     kv_bytes = cells * wl2.n_head_kv * wl2.head_dim * 2 * 2          # K and V, bf16
@@ -190,6 +204,18 @@ def main():
     flops3 = 4.0 * wl3.head_dim * wl3.n_head_q * n_cells
     gather3 = n_cells * wl3.n_head_kv * wl3.head_dim * 2 * 2
     tflops3 = flops3 / (ms_prefill * 1e-3) / 1e12
+
+    def sel_cells(wl):
+        n = 0
+        for r in range(wl.n_row):
+            ids = wl.sel[r]
+            ok = (ids >= 0) & (ids.astype(np.int64) * wl.block_size < wl.n_kv)
+            n += np.unique(ids[ok]).size * wl.block_size
+        return n
+
+    cells6 = sel_cells(wl6)
+    flops6 = 4.0 * wl6.head_dim * wl6.n_head_q * cells6
+    gather6 = cells6 * wl6.n_head_kv * wl6.head_dim * 2 * 2
 
     result = {
         "metric": "decode KV GB/s (% HBM peak) + sel-prefill TFLOP/s, GQA h256 at 32k depth",
@@ -219,6 +245,11 @@ def main():
                         "gathered_gbs": round(gather3 / (ms_prefill * 1e-3) / 1e9, 2),
                         "tokens_per_s": round(wl3.n_row / (ms_prefill * 1e-3), 1),
                         "prefill_path": sa.prefill_path(a3)},
+        "sel_decode": {"workload": f"16 rows x 512 block ids (4-cell blocks), 16/2 heads, D=256, bf16, "
+                                   f"N=32048, {SEL_DECODE_SPLITS} key-range splits + combine",
+                       "ms": round(ms_sd, 5), "tflops": round(flops6 / (ms_sd * 1e-3) / 1e12, 3),
+                       "gathered_gbs": round(gather6 / (ms_sd * 1e-3) / 1e9, 2),
+                       "tokens_per_s": round(wl6.n_row / (ms_sd * 1e-3), 1)},
         "copy_gbs": round(2 * copy_src.numel() * 4 / (ms_copy * 1e-3) / 1e9, 1),
         "tokens_per_s": round(wl2.n_stream / (ms_step * 1e-3), 1),
     }

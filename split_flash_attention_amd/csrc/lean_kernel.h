@@ -130,6 +130,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
 
     // ---- key slots --------------------------------------------------------------
     int n_keys, n_full = 0;
+    int id0 = 0;                               // selection: first list entry of this split
     if constexpr (MODE == kSel) {
         // the row's list: invalid ids become +inf, bitonic sort in LDS, then the
         // repeats are dropped by a wave-wide compaction (ballot + prefix count)
@@ -179,7 +180,17 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
             if (lane == 0) dst[0] = n_ids;
             for (int e = lane; e < n_ids; e += 64) dst[1 + e] = list[e];
         }
-        n_keys = n_ids * p.bs;
+        // A split covers cells [lo, hi): its ids are the sorted run from the first
+        // whose block ends after lo to the last whose block starts before hi.
+        int first = 0, last = 0;
+        for (int base = 0; base < n_ids; base += 64) {
+            const int e = base + lane;
+            const int64_t x = e < n_ids ? list[e] : 0x7fffffff;
+            first += __popcll(__ballot(e < n_ids && (x + 1) * p.bs <= lo));
+            last += __popcll(__ballot(e < n_ids && x * p.bs < hi));
+        }
+        id0 = first;
+        n_keys = max(0, last - first) * p.bs;
     } else {
         int lim_max = -1, lim_min = 0x7fffffff;
         const int m_end = min(p.M, m_wg + 16);
@@ -200,7 +211,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                 const int kslot = t0 + lane;
                 int c = -1;
                 if (kslot < n_keys) {
-                    const int id = list[kslot / p.bs];
+                    const int id = list[id0 + kslot / p.bs];
                     const int cc = id * p.bs + kslot % p.bs;
                     if (cc < p.n_kv && cc >= lo && cc < hi) c = cc;
                 }

@@ -87,3 +87,15 @@ def test_config4_semantic_edge_prefill_full(nan):
         assert np.isnan(np.delete(out, ex, axis=0)).all()
     else:
         assert np.isfinite(out).all()
+
+
+def test_selected_key_decode_full():
+    """The selected-key decode workload in the launch configuration bench.py times
+    (32 key-range splits + combine), against the oracle on every row."""
+    import bench
+    wl = gen.sel_decode()
+    out = hip_run.run_prefill(wl, n_splits=bench.SEL_DECODE_SPLITS)
+    assert np.isfinite(out).all()
+    ref = oracle.prefill(q=wl.q, k=wl.k, v=wl.v, kv_dtype="bf16", scale=wl.scale, q_pos=wl.q_pos,
+                         sel=wl.sel, block_size=wl.block_size)
+    nmse_check(out, ref, TOL["bf16"], "selected-key decode")

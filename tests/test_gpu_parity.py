@@ -294,6 +294,36 @@ def test_prefill_selection_splits():
         nmse_check(hip_run.run_prefill(wl, n_splits=n), ref, TOL["bf16"], f"splits {n}")
 
 
+@pytest.mark.parametrize("gqa", [(16, 4), (16, 2), (48, 4)])
+@pytest.mark.parametrize("n_splits", [1, 7, 16])
+def test_selected_key_decode(gqa, n_splits):
+    """Decode-shaped selection calls (16 rows, head dim 256, GQA 4 / 8 / 12): the key
+    range split over n_splits work-groups per row, partials merged by the combine;
+    each split visits exactly its share of the row's selected cells."""
+    hq, hkv = gqa
+    wl = gen.make_prefill_sel(seed=[21, hq // hkv, n_splits], n_row=16, n_head_q=hq, n_head_kv=hkv,
+                              head_dim=256, n_kv=3001, kv_dtype="bf16", n_sel=96, n_dup=9,
+                              n_invalid=5, block_size=4, first_pos=2985)
+    sel = wl.sel.copy()
+    sel[3] = -1                                   # a row with nothing valid
+    sel[5, :] = sel[5, 0]                         # a row with one block, repeated
+    wl.sel = sel
+    out, dev = hip_run.run_prefill(wl, n_splits=n_splits, dbg=True, return_dev=True)
+    ref = oracle_prefill(wl)
+    nmse_check(out, ref, TOL["bf16"], f"sel decode {gqa} splits {n_splits}")
+    assert np.all(out[3] == 0) and not np.signbit(out[3]).any()
+    # per split: the cells combined are the row's cells inside the split's range
+    cells, _ = oracle.visited_prefill(n_kv=wl.n_kv, n_head_kv=hkv, sel=wl.sel,
+                                      block_size=wl.block_size, rows=list(range(16)))
+    step = -(-wl.n_kv // n_splits)
+    dv = dev.dbg.cpu().numpy()
+    for r in range(16):
+        for t in range(n_splits):
+            c = cells[r][(cells[r] >= t * step) & (cells[r] < (t + 1) * step)]
+            for g in range(hkv):
+                assert dv[r, g, t].tolist() == [c.size, int(c.sum()), int((c * c).sum())], (r, g, t)
+
+
 def mask_small(nan=True, seed=15, **over):
     kw = dict(n_row=48, n_head_q=16, n_head_kv=4, head_dim=128, n_kv=700, kv_dtype="f16",
               causal=True, excluded_rows=3, nan_k=40 if nan else 0, softcap=30.0, alibi=True)

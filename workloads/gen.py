@@ -373,6 +373,17 @@ def config5(depth: int = 32000) -> DecodeWorkload:
                        causal=True, slice_len=2048, name=f"int8_verify_decode_d{depth}")
 
 
+def sel_decode(n_head_q: int = 16, n_head_kv: int = 2, n_kv: int = 32048) -> PrefillWorkload:
+    """Selected-key decode: 16 query rows (one new token of each of 16 sequences in one
+    unified cache) at the 16 newest positions, D=256, bf16, 512 ids per row over 4-cell
+    blocks (476 distinct valid + 26 duplicates + 10 invalid); run as the selection-mode
+    call with the key range split so that the rows fill the GPU."""
+    return make_prefill_sel(seed=[6, n_head_q // n_head_kv], n_row=16, n_head_q=n_head_q,
+                            n_head_kv=n_head_kv, head_dim=256, n_kv=n_kv, kv_dtype="bf16",
+                            n_sel=512, n_dup=26, n_invalid=10, block_size=4,
+                            first_pos=n_kv - 16, name="selected_key_decode_bf16")
+
+
 CONFIGS = {
     "1": config1,
     "2": config2,
@@ -381,4 +392,5 @@ CONFIGS = {
     "4c": lambda: config4(nan=False),
     "5a": lambda: config5(12000),
     "5b": lambda: config5(32000),
+    "sd": sel_decode,
 }
