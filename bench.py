@@ -15,7 +15,8 @@ key)), the selected-key decode (16 rows, one per sequence of a unified cache, wi
 the same lists and block size, the key range split 32 ways, then the combine),
 and a plain device copy of 1 GiB (the achievable copy rate, and the
 calibration for the memory counters).  `--verify` adds the int8 verify-window
-decode (16 streams x 16 rows, 48/4 heads, depth 32000, slices of 2048).
+decode (16 streams x 16 rows, 48/4 heads, depth 32000, slices of 2048) and the
+split-K decode with e4m3 K/V rows.
 
 Prints ONE JSON line.  Inputs are seeded synthetic data (no dataset).
 """
@@ -275,6 +276,23 @@ def main():
                                    "ms": round(ms5, 5), "gbs": round(bytes5 / (ms5 * 1e-3) / 1e9, 2),
                                    "tflops": round(flops5 / (ms5 * 1e-3) / 1e12, 2)}
         del d5
+        log("generating the split-K decode workload with e4m3 K/V")
+        wl2f = gen.config2(kv_dtype="fp8")
+        d2f = hip_run.DecodeDev(wl2f, "cuda", poison_outputs=False)
+        a2f, c2f = d2f.args(), d2f.combine_args()
+
+        def step2f():
+            sa.sel_attn_decode(a2f)
+            sa.sel_attn_split_combine(c2f)
+
+        step2f()
+        ms2f = timed(step2f, args.steps, torch)
+        bytes2f = cells * wl2f.n_head_kv * (wl2f.head_dim + 4) * 2         # e4m3 rows + fp32 scales
+        result["fp8_decode"] = {"workload": "split-K decode as above with e4m3 K/V rows + fp32 row scales",
+                                "ms": round(ms2f, 5), "gbs": round(bytes2f / (ms2f * 1e-3) / 1e9, 2),
+                                "hbm_peak_frac": round(bytes2f / (ms2f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                "tokens_per_s": round(wl2f.n_stream / (ms2f * 1e-3), 1)}
+        del d2f
 
     if not args.no_cpu_baseline:
         log("timing the FP64 oracle on a sample")

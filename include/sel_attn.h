@@ -67,6 +67,8 @@ extern "C" {
 #define SEL_ATTN_F16  1
 #define SEL_ATTN_BF16 2
 #define SEL_ATTN_I8   3 /* int8 rows, one fp32 scale per (cell, kv head) row */
+#define SEL_ATTN_FP8  4 /* e4m3 rows (maximum 448, no infinities, 0x7f/0xff NaN), one fp32
+                           scale per (cell, kv head) row (TensorFold PR #911: scale amax / 448) */
 
 /* op ids for sel_attn_supports */
 #define SEL_ATTN_OP_DECODE  1
@@ -98,7 +100,7 @@ extern "C" {
  *
  * Requirements (else EINVAL): non-null q, k, v, kv_len, part_o, part_ml;
  * positive sizes; n_head_q % n_head_kv == 0; slice_len > 0; cap > 0;
- * I8 needs k_scale and v_scale.  EUNSUPPORTED: head_dim not 64, 128 or 256;
+ * I8 and FP8 need k_scale and v_scale.  EUNSUPPORTED: head_dim not 64, 128 or 256;
  * unknown dtype; softcap < 0 or not finite; scale not finite; K/V, q or
  * part_o not 16-byte aligned.  EWORKSPACE: n_slices_max * slice_len < cap.
  */
@@ -108,10 +110,10 @@ typedef struct sel_attn_decode_args {
     const float* q;
     const void* k;
     const void* v;
-    int32_t kv_dtype;            /* SEL_ATTN_F32 / F16 / BF16 / I8 */
+    int32_t kv_dtype;            /* SEL_ATTN_F32 / F16 / BF16 / I8 / FP8 */
     int64_t kv_stride_stream, kv_stride_cell, kv_stride_head;
-    const float* k_scale;        /* I8 only */
-    const float* v_scale;        /* I8 only */
+    const float* k_scale;        /* I8 and FP8 only */
+    const float* v_scale;        /* I8 and FP8 only */
     int64_t sc_stride_stream, sc_stride_cell, sc_stride_head;
     const int32_t* kv_len;       /* [S] device */
     int32_t causal;

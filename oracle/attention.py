@@ -60,12 +60,31 @@ INF = float("inf")
 # storage -> float64
 # ----------------------------------------------------------------------------
 
+def e4m3_value(code):
+    """The real number an e4m3 byte stands for (format with maximum 448): sign
+    bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 gives
+    subnormals (m / 8) * 2^-6; codes 0x7f and 0xff are NaN; no infinities
+    (TensorFold PR #911: e4m3 rows, scale amax / 448)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
 def kv_to_f64(arr, dtype, scale=None):
     """Exact widening of K or V rows to float64.
 
     fp32 / fp16: the value itself.  bf16 (uint16 bits): the fp32 whose high
     half is those bits.  int8: q * scale, with the per-row fp32 scale
     broadcast over the last axis (exact in float64: 8 x 24 significant bits).
+    e4m3 (fp8): the byte's value times the row scale, likewise exact.
     """
     if dtype == "f32":
         return np.asarray(arr, dtype=np.float32).astype(np.float64)
@@ -76,6 +95,10 @@ def kv_to_f64(arr, dtype, scale=None):
         return bits.view(np.float32).astype(np.float64)
     if dtype == "i8":
         q = np.asarray(arr, dtype=np.int8).astype(np.float64)
+        s = np.asarray(scale, dtype=np.float32).astype(np.float64)
+        return q * s[..., None]
+    if dtype == "fp8":
+        q = E4M3_TABLE[np.asarray(arr, dtype=np.uint8)]
         s = np.asarray(scale, dtype=np.float32).astype(np.float64)
         return q * s[..., None]
     raise ValueError(f"unknown kv dtype {dtype!r}")

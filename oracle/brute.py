@@ -32,6 +32,15 @@ def _value(arr, idx, dtype, scale_arr=None, scale_idx=None):
     if dtype == "i8":
         s = struct.unpack("<f", struct.pack("<f", float(scale_arr[scale_idx])))[0]
         return int(x) * s
+    if dtype == "fp8":
+        # e4m3: sign, exponent (bias 7, field 0 subnormal), 3-bit mantissa; 0x7f/0xff NaN
+        s = struct.unpack("<f", struct.pack("<f", float(scale_arr[scale_idx])))[0]
+        c = int(x) & 0xFF
+        e, m = (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            return float("nan")
+        mag = math.ldexp(m, -9) if e == 0 else math.ldexp(8 + m, e - 10)
+        return (-mag if c & 0x80 else mag) * s
     raise ValueError(dtype)
 
 

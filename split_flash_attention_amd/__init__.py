@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libselattn.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
-F32, F16, BF16, I8 = 0, 1, 2, 3
+F32, F16, BF16, I8, FP8 = 0, 1, 2, 3, 4
 OP_DECODE, OP_PREFILL, OP_COMBINE = 1, 2, 3
 
 _i32, _i64, _f32, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
@@ -124,7 +124,8 @@ def _stream(stream) -> Optional[int]:
 
 def kv_dtype_code(t) -> int:
     import torch
-    m = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8}
+    m = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
+         torch.uint8: FP8, torch.float8_e4m3fn: FP8}        # uint8 holds e4m3 codes
     if t.dtype not in m:
         raise TypeError(f"unsupported K/V dtype {t.dtype}")
     return m[t.dtype]

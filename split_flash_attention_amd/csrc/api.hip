@@ -16,16 +16,21 @@ namespace {
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 
 bool dtype_ok(int dt) {
-    return dt == SEL_ATTN_F32 || dt == SEL_ATTN_F16 || dt == SEL_ATTN_BF16 || dt == SEL_ATTN_I8;
+    return dt == SEL_ATTN_F32 || dt == SEL_ATTN_F16 || dt == SEL_ATTN_BF16 || dt == SEL_ATTN_I8 ||
+           dt == SEL_ATTN_FP8;
 }
 
 int elem_bytes(int dt) {
     switch (dt) {
     case SEL_ATTN_F32: return 4;
-    case SEL_ATTN_I8: return 1;
+    case SEL_ATTN_I8:
+    case SEL_ATTN_FP8: return 1;
     default: return 2;
     }
 }
+
+// 1-byte rows that carry one fp32 scale per (cell, kv head) row
+bool scaled(int dt) { return dt == SEL_ATTN_I8 || dt == SEL_ATTN_FP8; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -45,8 +50,8 @@ int validate_decode(const sel_attn_decode_args* a) {
         return SEL_ATTN_EINVAL;
     if (a->n_head_q % a->n_head_kv != 0) return SEL_ATTN_EINVAL;
     if (!dtype_ok(a->kv_dtype)) return SEL_ATTN_EUNSUPPORTED;
-    if (a->kv_dtype == SEL_ATTN_I8 && (!a->k_scale || !a->v_scale)) return SEL_ATTN_EINVAL;
-    if (a->kv_dtype == SEL_ATTN_I8 &&
+    if (scaled(a->kv_dtype) && (!a->k_scale || !a->v_scale)) return SEL_ATTN_EINVAL;
+    if (scaled(a->kv_dtype) &&
         (a->sc_stride_stream < 0 || a->sc_stride_cell < 0 || a->sc_stride_head < 0))
         return SEL_ATTN_EINVAL;
     if (!head_dim_ok(a->head_dim)) return SEL_ATTN_EUNSUPPORTED;
@@ -87,8 +92,8 @@ int validate_prefill(const sel_attn_prefill_args* a) {
     if (a->n_splits == 1 && !a->out) return SEL_ATTN_EINVAL;
     if (a->n_splits > 1 && (!a->part_o || !a->part_ml)) return SEL_ATTN_EINVAL;
     if (!dtype_ok(a->kv_dtype)) return SEL_ATTN_EUNSUPPORTED;
-    if (a->kv_dtype == SEL_ATTN_I8 && (!a->k_scale || !a->v_scale)) return SEL_ATTN_EINVAL;
-    if (a->kv_dtype == SEL_ATTN_I8 && (a->sc_stride_cell < 0 || a->sc_stride_head < 0))
+    if (scaled(a->kv_dtype) && (!a->k_scale || !a->v_scale)) return SEL_ATTN_EINVAL;
+    if (scaled(a->kv_dtype) && (a->sc_stride_cell < 0 || a->sc_stride_head < 0))
         return SEL_ATTN_EINVAL;
     if ((a->alibi_slopes || (a->mask && a->causal)) && !a->q_pos) return SEL_ATTN_EINVAL;
     if (a->sel) {

@@ -24,12 +24,25 @@ __device__ __forceinline__ float f16_to_f32(uint16_t x) {
     return __half2float(__ushort_as_half(x));
 }
 
-// Widen element i of a K/V row of storage type `dt`.
+// e4m3 byte -> fp32 (exact): sign, exponent field with bias 7 (0: subnormal
+// m * 2^-9), 3 mantissa bits, 0x7f / 0xff NaN, no infinities.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+    float mag;
+    if (e == 15u && m == 7u) mag = __builtin_nanf("");
+    else if (e == 0u) mag = static_cast<float>(m) * 0x1p-9f;
+    else mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// Widen element i of a K/V row of storage type `dt` (the row scale of int8 and
+// e4m3 rows is applied by the caller).
 __device__ __forceinline__ float load_kv_elem(const void* base, int64_t idx, int dt) {
     switch (dt) {
     case SEL_ATTN_F32: return static_cast<const float*>(base)[idx];
     case SEL_ATTN_F16: return f16_to_f32(static_cast<const uint16_t*>(base)[idx]);
     case SEL_ATTN_BF16: return bf16_to_f32(static_cast<const uint16_t*>(base)[idx]);
+    case SEL_ATTN_FP8: return e4m3_to_f32(static_cast<const uint8_t*>(base)[idx]);
     default: return static_cast<float>(static_cast<const int8_t*>(base)[idx]);
     }
 }

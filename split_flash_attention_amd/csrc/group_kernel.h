@@ -35,17 +35,17 @@ template <int KT, int D, int W>
 __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, const int gy, const int b,
                                            char* smem) {
     constexpr bool F16 = (KT == SEL_ATTN_F16);
-    constexpr bool I8 = (KT == SEL_ATTN_I8);
+    constexpr bool B8 = byte_kv(KT);       // int8 or e4m3 rows with row scales
     constexpr int NKK = D / 32;                  // contraction steps of S^T
     constexpr int NDB = D / 16;                  // dim blocks of O^T
-    constexpr int GCH = I8 ? D / 16 : D / 8;     // 16-byte chunks per K/V row in memory
+    constexpr int GCH = B8 ? D / 16 : D / 8;     // 16-byte chunks per K/V row in memory
     constexpr int NT = 64 * W;
     constexpr int K_TASKS = kTK * GCH;           // task e < K_TASKS: K row e / GCH, chunk e % GCH
     constexpr int V_TASKS = 8 * 2 * GCH;         // keys 4 * (e' & 7) + 0..3, 8-byte half chunk e' >> 3
     constexpr int TASKS = K_TASKS + V_TASKS;
     constexpr int NSLOT = (TASKS + NT - 1) / NT;
-    constexpr int EPH = I8 ? 8 : 4;              // elements per 8-byte half chunk
-    constexpr int ROWB = D * (I8 ? 1 : 2);
+    constexpr int EPH = B8 ? 8 : 4;              // elements per 8-byte half chunk
+    constexpr int ROWB = D * (B8 ? 1 : 2);
     static_assert(K_TASKS % 64 == 0 && V_TASKS % 64 == 0, "tasks must fill whole waves");
 
     char* k_lds = smem;                                            // kTK * D * 2
@@ -125,11 +125,11 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     // Buffer loads through a descriptor that starts at the unit's first key row and
     // ends with its last needed row: rows past it (the tail of the last tile) read
     // as zeros.  32-bit offsets: slice_len * cell stride < 2^31 is checked on the host.
-    const int cb = static_cast<int>(p.kv_sc * (I8 ? 1 : 2));
+    const int cb = static_cast<int>(p.kv_sc * (B8 ? 1 : 2));
     const int64_t kv_base = static_cast<int64_t>(b) * p.kv_ss + static_cast<int64_t>(g) * p.kv_sh;
     const int64_t sc_base = static_cast<int64_t>(b) * p.sc_ss + static_cast<int64_t>(g) * p.sc_sh;
-    const char* kbase = static_cast<const char*>(p.k) + (kv_base + static_cast<int64_t>(lo) * p.kv_sc) * (I8 ? 1 : 2);
-    const char* vbase = static_cast<const char*>(p.v) + (kv_base + static_cast<int64_t>(lo) * p.kv_sc) * (I8 ? 1 : 2);
+    const char* kbase = static_cast<const char*>(p.k) + (kv_base + static_cast<int64_t>(lo) * p.kv_sc) * (B8 ? 1 : 2);
+    const char* vbase = static_cast<const char*>(p.v) + (kv_base + static_cast<int64_t>(lo) * p.kv_sc) * (B8 ? 1 : 2);
     const int nrec = n_keys > 0 ? (n_keys - 1) * cb + ROWB : 0;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), static_cast<short>(0), nrec, 0x00020000);
@@ -168,7 +168,7 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                 rg.v[i][1] = u32x4{a2[0], a2[1], a3[0], a3[1]};
             }
         }
-        if constexpr (I8) {
+        if constexpr (B8) {
             if (tid < kTK) {
                 const bool in = t0 + tid < n_keys;
                 const int64_t si = sc_base + static_cast<int64_t>(lo + t0 + tid) * p.sc_sc;
@@ -183,15 +183,15 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
             const int e = tid + i * NT;
             if (e < K_TASKS) {
                 const int key = e / GCH, ch = e % GCH;
-                if constexpr (I8) {
+                if constexpr (B8) {
                     const u32x4 rw = rg.k[i];
                     u32x4 w0, w1;
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        w0[2 * j] = i8pair_bf16(rw[j], 0, rw[j], 1);
-                        w0[2 * j + 1] = i8pair_bf16(rw[j], 2, rw[j], 3);
-                        w1[2 * j] = i8pair_bf16(rw[2 + j], 0, rw[2 + j], 1);
-                        w1[2 * j + 1] = i8pair_bf16(rw[2 + j], 2, rw[2 + j], 3);
+                        w0[2 * j] = bpair_bf16<KT>(rw[j], 0, rw[j], 1);
+                        w0[2 * j + 1] = bpair_bf16<KT>(rw[j], 2, rw[j], 3);
+                        w1[2 * j] = bpair_bf16<KT>(rw[2 + j], 0, rw[2 + j], 1);
+                        w1[2 * j + 1] = bpair_bf16<KT>(rw[2 + j], 2, rw[2 + j], 3);
                     }
                     *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch, D)) = w0;
                     *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch + 1, D)) = w1;
@@ -209,7 +209,7 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                     w[j][0] = rg.v[i][j >> 1][2 * (j & 1)];
                     w[j][1] = rg.v[i][j >> 1][2 * (j & 1) + 1];
                 }
-                if constexpr (I8) {
+                if constexpr (B8) {
                     // dims hc * 8 + 4 * h + jj (byte jj of word h of each key).  Their
                     // V^T rows are hc * 8 + 4 * h + (jj ^ c), c = hc & 3, and the chunk
                     // swizzle depends on h only: the address is a per-half base with
@@ -221,8 +221,8 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                         const int wbc = (hc * 8 + 4 * h + c) * 64 + ((gq ^ ((2 * hc + h) & 3)) << 4) + 8 * kb;
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj) {
-                            const uint32_t lo2 = i8pair_bf16(w[0][h], jj, w[1][h], jj);
-                            const uint32_t hi2 = i8pair_bf16(w[2][h], jj, w[3][h], jj);
+                            const uint32_t lo2 = bpair_bf16<KT>(w[0][h], jj, w[1][h], jj);
+                            const uint32_t hi2 = bpair_bf16<KT>(w[2][h], jj, w[3][h], jj);
                             *reinterpret_cast<uint2*>(vt_lds + (wbc ^ (jj << 6))) = uint2{lo2, hi2};
                         }
                     }
@@ -245,7 +245,7 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                 }
             }
         }
-        if constexpr (I8) {
+        if constexpr (B8) {
             if (tid < kTK) {
                 ksc_lds[tid] = rg.ks;
                 vsc_lds[tid] = rg.vs;
@@ -296,7 +296,7 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         float sc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) sc[e] = s[e >> 2][e & 3];
-        if constexpr (I8) {
+        if constexpr (B8) {
             const float4 k0 = *reinterpret_cast<const float4*>(ksc_lds + 4 * lg);
             const float4 k1 = *reinterpret_cast<const float4*>(ksc_lds + 16 + 4 * lg);
             sc[0] *= k0.x; sc[1] *= k0.y; sc[2] *= k0.z; sc[3] *= k0.w;
@@ -364,7 +364,7 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) l_run += pv[e];
-        if constexpr (I8) {
+        if constexpr (B8) {
             const float4 v0 = *reinterpret_cast<const float4*>(vsc_lds + 4 * lg);
             const float4 v1 = *reinterpret_cast<const float4*>(vsc_lds + 16 + 4 * lg);
             pv[0] *= v0.x; pv[1] *= v0.y; pv[2] *= v0.z; pv[3] *= v0.w;
@@ -514,8 +514,11 @@ inline hipError_t group_launch(int dt, const MParams& p, dim3 grid, int w, hipSt
     if (dt == SEL_ATTN_F16)
         return p.D == 256 ? group_launch_w<SEL_ATTN_F16, 256>(p, grid, w, st)
                           : group_launch_w<SEL_ATTN_F16, 128>(p, grid, w, st);
-    return p.D == 256 ? group_launch_w<SEL_ATTN_I8, 256>(p, grid, w, st)
-                      : group_launch_w<SEL_ATTN_I8, 128>(p, grid, w, st);
+    if (dt == SEL_ATTN_I8)
+        return p.D == 256 ? group_launch_w<SEL_ATTN_I8, 256>(p, grid, w, st)
+                          : group_launch_w<SEL_ATTN_I8, 128>(p, grid, w, st);
+    return p.D == 256 ? group_launch_w<SEL_ATTN_FP8, 256>(p, grid, w, st)
+                      : group_launch_w<SEL_ATTN_FP8, 128>(p, grid, w, st);
 }
 
 }  // namespace mk

@@ -47,15 +47,15 @@ template <int MODE, int KT, int D, int CP>
 __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, const int gy, const int bz,
                                           char* smem) {
     constexpr bool F16 = (KT == SEL_ATTN_F16);
-    constexpr bool I8 = (KT == SEL_ATTN_I8);
+    constexpr bool B8 = byte_kv(KT);       // int8 or e4m3 rows with row scales
     constexpr int NKK = D / 32;
     constexpr int NDB = D / 16;
-    constexpr int GCH = I8 ? D / 16 : D / 8;        // 16-byte chunks per K/V row in memory
+    constexpr int GCH = B8 ? D / 16 : D / 8;        // 16-byte chunks per K/V row in memory
     constexpr int K_TASKS = kLT * GCH;              // one 16-byte load each
     constexpr int V_TASKS = 4 * GCH;                // task e: keys 4*(e & 3) + 0..3, chunk e >> 2
     constexpr int NKL = (K_TASKS + 63) / 64;
     constexpr int NVL = (V_TASKS + 63) / 64;
-    constexpr int EPC = I8 ? 16 : 8;
+    constexpr int EPC = B8 ? 16 : 8;
 
     char* k_lds = smem;
     char* vt_lds = smem + kLT * D * 2;
@@ -229,10 +229,10 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     // the rows past it (the tail of the last tile) read as zeros without a test;
     // in selection mode it covers the whole cache and an absent cell gets an offset
     // past the end.  Offsets are 32-bit (cell stride * cells < 2^31, checked on the host).
-    constexpr int ROWB = D * (I8 ? 1 : 2);
-    const int cb = static_cast<int>(p.kv_sc * (I8 ? 1 : 2));
-    const char* kbase = static_cast<const char*>(p.k) + kv_base * (I8 ? 1 : 2);
-    const char* vbase = static_cast<const char*>(p.v) + kv_base * (I8 ? 1 : 2);
+    constexpr int ROWB = D * (B8 ? 1 : 2);
+    const int cb = static_cast<int>(p.kv_sc * (B8 ? 1 : 2));
+    const char* kbase = static_cast<const char*>(p.k) + kv_base * (B8 ? 1 : 2);
+    const char* vbase = static_cast<const char*>(p.v) + kv_base * (B8 ? 1 : 2);
     int nrec;
     if constexpr (MODE == kSel) {
         nrec = (p.n_kv - 1) * cb + ROWB;
@@ -287,7 +287,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                 }
             }
         }
-        if constexpr (I8) {
+        if constexpr (B8) {
             if (lane < kLT) {
                 int cell;
                 if constexpr (MODE == kSel) cell = tc[lane];
@@ -303,15 +303,15 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
             const int e = lane + 64 * i;
             if (e < K_TASKS) {
                 const int key = e / GCH, ch = e % GCH;
-                if constexpr (I8) {
+                if constexpr (B8) {
                     const u32x4 rw = kreg[i];
                     u32x4 w0, w1;
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        w0[2 * j] = i8pair_bf16(rw[j], 0, rw[j], 1);
-                        w0[2 * j + 1] = i8pair_bf16(rw[j], 2, rw[j], 3);
-                        w1[2 * j] = i8pair_bf16(rw[2 + j], 0, rw[2 + j], 1);
-                        w1[2 * j + 1] = i8pair_bf16(rw[2 + j], 2, rw[2 + j], 3);
+                        w0[2 * j] = bpair_bf16<KT>(rw[j], 0, rw[j], 1);
+                        w0[2 * j + 1] = bpair_bf16<KT>(rw[j], 2, rw[j], 3);
+                        w1[2 * j] = bpair_bf16<KT>(rw[2 + j], 0, rw[2 + j], 1);
+                        w1[2 * j + 1] = bpair_bf16<KT>(rw[2 + j], 2, rw[2 + j], 3);
                     }
                     *reinterpret_cast<u32x4*>(k_lds + k16_off(key, 2 * ch, D)) = w0;
                     *reinterpret_cast<u32x4*>(k_lds + k16_off(key, 2 * ch + 1, D)) = w1;
@@ -328,10 +328,10 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
 #pragma unroll
                 for (int dd = 0; dd < EPC; ++dd) {
                     uint32_t lo2, hi2;
-                    if constexpr (I8) {
+                    if constexpr (B8) {
                         const int w = dd >> 2, by = dd & 3;
-                        lo2 = i8pair_bf16(vreg[i][0][w], by, vreg[i][1][w], by);
-                        hi2 = i8pair_bf16(vreg[i][2][w], by, vreg[i][3][w], by);
+                        lo2 = bpair_bf16<KT>(vreg[i][0][w], by, vreg[i][1][w], by);
+                        hi2 = bpair_bf16<KT>(vreg[i][2][w], by, vreg[i][3][w], by);
                     } else {
                         const int w = dd >> 1;
                         if (dd & 1) {
@@ -346,7 +346,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                 }
             }
         }
-        if constexpr (I8) {
+        if constexpr (B8) {
             if (lane < kLT) {
                 ksc_lds[lane] = kscr;
                 vsc_lds[lane] = vscr;
@@ -413,7 +413,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
 #pragma unroll
         for (int i = 0; i < 4; ++i) vis[i] = full || (cell[i] >= 0 && cell[i] < lim);
         float sc[4] = {s[0], s[1], s[2], s[3]};
-        if constexpr (I8) {
+        if constexpr (B8) {
             const float4 k4 = *reinterpret_cast<const float4*>(ksc_lds + 4 * lg);
             sc[0] *= k4.x; sc[1] *= k4.y; sc[2] *= k4.z; sc[3] *= k4.w;
         }
@@ -462,7 +462,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
             pe[i] = vis[i] ? __builtin_amdgcn_exp2f(fmaf(sc[i], kLog2e, -mls)) : 0.f;
             l_run += pe[i];
         }
-        if constexpr (I8) {
+        if constexpr (B8) {
             const float4 v4 = *reinterpret_cast<const float4*>(vsc_lds + 4 * lg);
             pe[0] *= v4.x; pe[1] *= v4.y; pe[2] *= v4.z; pe[3] *= v4.w;
         }
@@ -582,7 +582,8 @@ template <int MODE, int CP>
 hipError_t lean_launch_dt(int dt, const MParams& p, dim3 grid, hipStream_t st) {
     if (dt == SEL_ATTN_BF16) return lean_launch_dim<MODE, SEL_ATTN_BF16, CP>(p, grid, st);
     if (dt == SEL_ATTN_F16) return lean_launch_dim<MODE, SEL_ATTN_F16, CP>(p, grid, st);
-    return lean_launch_dim<MODE, SEL_ATTN_I8, CP>(p, grid, st);
+    if (dt == SEL_ATTN_I8) return lean_launch_dim<MODE, SEL_ATTN_I8, CP>(p, grid, st);
+    return lean_launch_dim<MODE, SEL_ATTN_FP8, CP>(p, grid, st);
 }
 
 // Decode streams each unit with non-temporal loads when one work-group reads it

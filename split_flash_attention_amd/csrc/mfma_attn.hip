@@ -4,7 +4,9 @@
 namespace selattn {
 
 namespace {
-bool dtype_ok(int dt) { return dt == SEL_ATTN_BF16 || dt == SEL_ATTN_F16 || dt == SEL_ATTN_I8; }
+bool dtype_ok(int dt) {
+    return dt == SEL_ATTN_BF16 || dt == SEL_ATTN_F16 || dt == SEL_ATTN_I8 || dt == SEL_ATTN_FP8;
+}
 }  // namespace
 
 bool mfma_decode_eligible(const sel_attn_decode_args& a) {

@@ -27,7 +27,7 @@ hipError_t launch_mfma_decode(const sel_attn_decode_args& a, hipStream_t st) {
     p.n_units_x = n_sl;
     p.n_units_z = a.n_stream;
     // the single-wave and group kernels address a unit's rows with 32-bit buffer offsets
-    const int64_t cell_bytes = a.kv_stride_cell * (a.kv_dtype == SEL_ATTN_I8 ? 1 : 2);
+    const int64_t cell_bytes = a.kv_stride_cell * (a.kv_dtype == SEL_ATTN_I8 || a.kv_dtype == SEL_ATTN_FP8 ? 1 : 2);
     const bool off32 = static_cast<int64_t>(a.cap) * cell_bytes < (int64_t{1} << 31) - 64;
     const int nqb = (p.M + 15) / 16;
     if (off32 && nqb <= 1) {

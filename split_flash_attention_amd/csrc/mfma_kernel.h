@@ -91,16 +91,32 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-// int8 byte `byte` of `word` as a float (exact)
-__device__ __forceinline__ float i8_float(uint32_t word, int byte) {
-    return static_cast<float>(static_cast<int8_t>((word >> (8 * byte)) & 0xffu));
+// 1-byte K/V rows with one fp32 scale per row: int8 or e4m3
+constexpr bool byte_kv(int kt) { return kt == SEL_ATTN_I8 || kt == SEL_ATTN_FP8; }
+
+// byte `byte` of `word` as a float (exact): int8 by a sign-extending convert,
+// e4m3 by the matrix-core unit's fp8 convert (v_cvt_f32_fp8, byte select)
+template <int KT>
+__device__ __forceinline__ float byte_float(uint32_t word, int byte) {
+    if constexpr (KT == SEL_ATTN_FP8) {
+        switch (byte) {
+        case 0: return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), 0);
+        case 1: return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), 1);
+        case 2: return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), 2);
+        default: return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), 3);
+        }
+    } else {
+        return static_cast<float>(static_cast<int8_t>((word >> (8 * byte)) & 0xffu));
+    }
 }
 
-// bf16 pair {bytes (wa, ba), (wb, bb)} of int8 data: an int8 value fits 8
-// significant bits, so the high half of its float is its exact bf16; one
-// v_perm_b32 takes both high halves
-__device__ __forceinline__ uint32_t i8pair_bf16(uint32_t wa, int ba, uint32_t wb, int bb) {
-    return __builtin_amdgcn_perm(__float_as_uint(i8_float(wb, bb)), __float_as_uint(i8_float(wa, ba)), 0x07060302u);
+// bf16 pair {bytes (wa, ba), (wb, bb)} of int8 or e4m3 data: both fit 8
+// significant bits (e4m3: 4), so the high half of the float is the exact bf16;
+// one v_perm_b32 takes both high halves
+template <int KT>
+__device__ __forceinline__ uint32_t bpair_bf16(uint32_t wa, int ba, uint32_t wb, int bb) {
+    return __builtin_amdgcn_perm(__float_as_uint(byte_float<KT>(wb, bb)),
+                                 __float_as_uint(byte_float<KT>(wa, ba)), 0x07060302u);
 }
 
 // byte offset of 16-byte chunk `ch` (8 dims) of key row `key` in the K tile; chunks
@@ -133,17 +149,17 @@ template <int MODE, int KT, int D, int QB, int W>
 __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, const int gy, const int bz,
                                           char* smem, int& s_nids) {
     constexpr bool F16 = (KT == SEL_ATTN_F16);
-    constexpr bool I8 = (KT == SEL_ATTN_I8);
+    constexpr bool B8 = byte_kv(KT);       // int8 or e4m3 rows with row scales
     constexpr int NKK = D / 32;                  // contraction steps for S^T
     constexpr int NDB = D / 16;                  // dim blocks of O^T
-    constexpr int GCH = I8 ? D / 16 : D / 8;     // 16-byte chunks per K/V row in memory
+    constexpr int GCH = B8 ? D / 16 : D / 8;     // 16-byte chunks per K/V row in memory
     constexpr int NT = 64 * W;
     constexpr int K_TASKS = kTK * GCH;           // one 16-byte load each
     constexpr int V_TASKS = 8 * GCH;             // four 16-byte loads each: task e covers
                                                  // keys 4*(e & 7) + 0..3, chunk e >> 3
     constexpr int NKL = (K_TASKS + NT - 1) / NT;
     constexpr int NVL = (V_TASKS + NT - 1) / NT;
-    constexpr int EPC = I8 ? 16 : 8;             // elements per 16-byte chunk
+    constexpr int EPC = B8 ? 16 : 8;             // elements per 16-byte chunk
 
     char* k_lds = smem;                                            // kTK * D * 2
     char* vt_lds = smem + kTK * D * 2;                             // D * 64
@@ -313,9 +329,9 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                             static_cast<int64_t>(g) * p.kv_sh;
     const int64_t sc_base = (MODE == kDecode ? static_cast<int64_t>(b) * p.sc_ss : 0) +
                             static_cast<int64_t>(g) * p.sc_sh;
-    const char* kbase = static_cast<const char*>(p.k) + kv_base * (I8 ? 1 : 2);
-    const char* vbase = static_cast<const char*>(p.v) + kv_base * (I8 ? 1 : 2);
-    const int64_t cell_bytes = p.kv_sc * (I8 ? 1 : 2);
+    const char* kbase = static_cast<const char*>(p.k) + kv_base * (B8 ? 1 : 2);
+    const char* vbase = static_cast<const char*>(p.v) + kv_base * (B8 ? 1 : 2);
+    const int64_t cell_bytes = p.kv_sc * (B8 ? 1 : 2);
 
     // ---- tile loads into registers -----------------------------------------
     u32x4 kreg[NKL];
@@ -345,7 +361,7 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                 }
             }
         }
-        if constexpr (I8) {
+        if constexpr (B8) {
             if (tid < kTK) {
                 const int cell = slot_cell(t0 + tid);
                 kscr = cell >= 0 ? p.ksc[sc_base + cell * p.sc_sc] : 0.f;
@@ -360,15 +376,15 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
             const int e = tid + i * NT;
             if (e < K_TASKS) {
                 const int key = e / GCH, ch = e % GCH;
-                if constexpr (I8) {
+                if constexpr (B8) {
                     const u32x4 r = kreg[i];
                     u32x4 w0, w1;
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        w0[2 * j] = i8pair_bf16(r[j], 0, r[j], 1);
-                        w0[2 * j + 1] = i8pair_bf16(r[j], 2, r[j], 3);
-                        w1[2 * j] = i8pair_bf16(r[2 + j], 0, r[2 + j], 1);
-                        w1[2 * j + 1] = i8pair_bf16(r[2 + j], 2, r[2 + j], 3);
+                        w0[2 * j] = bpair_bf16<KT>(r[j], 0, r[j], 1);
+                        w0[2 * j + 1] = bpair_bf16<KT>(r[j], 2, r[j], 3);
+                        w1[2 * j] = bpair_bf16<KT>(r[2 + j], 0, r[2 + j], 1);
+                        w1[2 * j + 1] = bpair_bf16<KT>(r[2 + j], 2, r[2 + j], 3);
                     }
                     *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch, D)) = w0;
                     *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch + 1, D)) = w1;
@@ -386,10 +402,10 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
 #pragma unroll
                 for (int dd = 0; dd < EPC; ++dd) {
                     uint32_t lo2, hi2;
-                    if constexpr (I8) {
+                    if constexpr (B8) {
                         const int w = dd >> 2, by = dd & 3;
-                        lo2 = i8pair_bf16(vreg[i][0][w], by, vreg[i][1][w], by);
-                        hi2 = i8pair_bf16(vreg[i][2][w], by, vreg[i][3][w], by);
+                        lo2 = bpair_bf16<KT>(vreg[i][0][w], by, vreg[i][1][w], by);
+                        hi2 = bpair_bf16<KT>(vreg[i][2][w], by, vreg[i][3][w], by);
                     } else {
                         const int w = dd >> 1;
                         if (dd & 1) {
@@ -404,7 +420,7 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                 }
             }
         }
-        if constexpr (I8) {
+        if constexpr (B8) {
             if (tid < kTK) {
                 ksc_lds[tid] = kscr;
                 vsc_lds[tid] = vscr;
@@ -473,7 +489,7 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                     }
                 }
                 float x = s[k][kb][i];
-                if constexpr (I8) x *= ksc_lds[kb * 16 + 4 * lg + i];
+                if constexpr (B8) x *= ksc_lds[kb * 16 + 4 * lg + i];
                 if (p.softcap > 0.f) x = p.softcap * tanhf(x / p.softcap);
                 x += slope[k] * static_cast<float>(cell - qv_pos[k]);
                 x += maskv;
@@ -510,7 +526,7 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float w = pe[e];
-                if constexpr (I8) w *= vsc_lds[(e >> 2) * 16 + 4 * lg + (e & 3)];
+                if constexpr (B8) w *= vsc_lds[(e >> 2) * 16 + 4 * lg + (e & 3)];
                 pv[e] = w;
             }
             pop[k] = u32x4{pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]),
@@ -743,8 +759,11 @@ hipError_t launch_mode(int dt, const MParams& p, dim3 grid, Shape sh, hipStream_
     if (dt == SEL_ATTN_F16)
         return p.D == 256 ? launch_shape<MODE, SEL_ATTN_F16, 256>(p, grid, sh, st)
                           : launch_shape<MODE, SEL_ATTN_F16, 128>(p, grid, sh, st);
-    return p.D == 256 ? launch_shape<MODE, SEL_ATTN_I8, 256>(p, grid, sh, st)
-                      : launch_shape<MODE, SEL_ATTN_I8, 128>(p, grid, sh, st);
+    if (dt == SEL_ATTN_I8)
+        return p.D == 256 ? launch_shape<MODE, SEL_ATTN_I8, 256>(p, grid, sh, st)
+                          : launch_shape<MODE, SEL_ATTN_I8, 128>(p, grid, sh, st);
+    return p.D == 256 ? launch_shape<MODE, SEL_ATTN_FP8, 256>(p, grid, sh, st)
+                      : launch_shape<MODE, SEL_ATTN_FP8, 128>(p, grid, sh, st);
 }
 
 }  // namespace mk

@@ -45,7 +45,7 @@ hipError_t launch_mfma_prefill_sel(const sel_attn_prefill_args& a, hipStream_t s
     p.sel = a.sel; p.n_sel = a.n_sel; p.bs = a.block_size; p.sel_pow2 = next_pow2(a.n_sel);
     const int nqc = (p.M + p.qpw - 1) / p.qpw;
     dim3 grid(a.n_splits, a.n_head_kv * nqc, a.n_row);
-    const int64_t span = static_cast<int64_t>(a.n_kv) * a.kv_stride_cell * (a.kv_dtype == SEL_ATTN_I8 ? 1 : 2);
+    const int64_t span = static_cast<int64_t>(a.n_kv) * a.kv_stride_cell * (a.kv_dtype == SEL_ATTN_I8 || a.kv_dtype == SEL_ATTN_FP8 ? 1 : 2);
     if (span < (int64_t{1} << 31) - 64) {
         p.qpw = 16;
         const int nqc16 = (p.M + 15) / 16;

@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
                                      static_cast<int64_t>(g) * p.kv_sh;
                 kx = load_kv_elem(p.k, base + d, p.dt);
                 vx = load_kv_elem(p.v, base + d, p.dt);
-                if (p.dt == SEL_ATTN_I8) {
+                if (p.dt == SEL_ATTN_I8 || p.dt == SEL_ATTN_FP8) {
                     const int64_t sb = (p.mode == kDecode ? static_cast<int64_t>(b) * p.sc_ss : 0) +
                                        static_cast<int64_t>(c) * p.sc_sc +
                                        static_cast<int64_t>(g) * p.sc_sh;

@@ -21,6 +21,8 @@ def kv_tensor(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
         return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
     if dtype == "i8":
         return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+    if dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.uint8)).to(device)
     raise ValueError(dtype)
 
 

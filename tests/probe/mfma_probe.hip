@@ -1,4 +1,5 @@
-// One-wave probe of the v_mfma_f32_16x16x32_{bf16,f16} lane layout on gfx950.
+// One-wave probes on gfx950: the v_mfma_f32_16x16x32_{bf16,f16} lane layout, and
+// the e4m3 byte convert (below).
 // Each lane passes its own 8 A values and 8 B values (16-bit bit patterns) and
 // gets back its 4 accumulator values; the test checks them against the layout
 // the attention kernels assume.  Buffers: a, b [64][8] uint16; d [64][4] float.
@@ -28,5 +29,22 @@ extern "C" int mfma_probe(const void* a, const void* b, void* d, int f16, void* 
     hipLaunchKernelGGL(probe, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
                        static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
                        static_cast<float*>(d), f16);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// e4m3 decoding probe: lane l converts the four bytes of word l with the
+// v_cvt_f32_fp8 byte-select forms the kernels use; out [64][4] floats.
+__global__ void __launch_bounds__(64) fp8_cvt(const uint32_t* w, float* out) {
+    const int l = threadIdx.x;
+    const int x = static_cast<int>(w[l]);
+    out[l * 4 + 0] = __builtin_amdgcn_cvt_f32_fp8(x, 0);
+    out[l * 4 + 1] = __builtin_amdgcn_cvt_f32_fp8(x, 1);
+    out[l * 4 + 2] = __builtin_amdgcn_cvt_f32_fp8(x, 2);
+    out[l * 4 + 3] = __builtin_amdgcn_cvt_f32_fp8(x, 3);
+}
+
+extern "C" int fp8_probe(const void* w, void* out, void* stream) {
+    hipLaunchKernelGGL(fp8_cvt, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint32_t*>(w), static_cast<float*>(out));
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -91,6 +91,12 @@ def test_good_arguments_are_supported(L):
     assert sa.supports(sa.OP_PREFILL, good_prefill())
     assert sa.supports(sa.OP_COMBINE, good_combine())
     assert not sa.supports(99, good_decode())
+    # one-byte rows with fp32 row scales: int8 and e4m3 (fp8)
+    for dt in (sa.I8, sa.FP8):
+        a = good_decode(kv_dtype=dt, k_scale=FAKE, v_scale=FAKE, kv_stride_stream=32768 * 1024,
+                        kv_stride_cell=1024, kv_stride_head=256)
+        assert sa.supports(sa.OP_DECODE, a)
+        assert sa.decode_path(a) == 1                        # the matrix-core kernels take it
 
 
 @pytest.mark.parametrize("over,code", [
@@ -101,6 +107,8 @@ def test_good_arguments_are_supported(L):
     (dict(n_head_q=30), sa.EINVAL),            # 30 % 4 != 0
     (dict(slice_len=0), sa.EINVAL),
     (dict(kv_dtype=sa.I8), sa.EINVAL),         # int8 without scales
+    (dict(kv_dtype=sa.FP8), sa.EINVAL),        # e4m3 without scales
+    (dict(kv_dtype=5), sa.EUNSUPPORTED),       # no storage type 5
     (dict(head_dim=96, kv_stride_head=96), sa.EUNSUPPORTED),
     (dict(kv_dtype=7), sa.EUNSUPPORTED),
     (dict(softcap=-1.0), sa.EUNSUPPORTED),

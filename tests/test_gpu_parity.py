@@ -17,7 +17,7 @@ from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-6, "f16": 5e-5, "bf16": 5e-5, "i8": 5e-5}
+TOL = {"f32": 1e-6, "f16": 5e-5, "bf16": 5e-5, "i8": 5e-5, "fp8": 5e-5}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -97,6 +97,11 @@ DECODE_CASES = {
                                         softcap=20.0, alibi=True),
     "bf16_verify_two_chunks": dict(n_stream=2, n_row=16, n_head_q=16, n_head_kv=1, head_dim=256,
                                    cap=600, kv_dtype="bf16", depths=[600, 100], slice_len=256),
+    # e4m3 K/V rows with fp32 row scales: one block per unit, and a work-group unit
+    "fp8_gqa8_d256": dict(n_stream=2, n_row=1, n_head_q=32, n_head_kv=4, head_dim=256,
+                          cap=1800, kv_dtype="fp8", depths=[1800, 700], slice_len=512),
+    "fp8_verify_gqa12_d128": dict(n_stream=2, n_row=8, n_head_q=24, n_head_kv=2, head_dim=128,
+                                  cap=900, kv_dtype="fp8", depths=[900, 333], slice_len=256),
     "i8_verify_noncausal_d128": dict(n_stream=2, n_row=7, n_head_q=24, n_head_kv=2, head_dim=128,
                                      cap=900, kv_dtype="i8", depths=[900, 250], slice_len=384,
                                      causal=False),
@@ -184,21 +189,24 @@ def test_decode_empty_rows_are_zero():
     assert np.all(out[1, :2] == 0)
 
 
-@pytest.mark.parametrize("kind", ["one_block_bf16", "work_group_bf16", "work_group_i8"])
+@pytest.mark.parametrize("kind", ["one_block_bf16", "work_group_bf16", "work_group_i8", "work_group_fp8"])
 def test_decode_nan_propagation(kind):
     """A NaN key element (or int8 key scale) makes exactly the query vectors that
     see that key NaN; causal rows that cannot see it stay finite."""
     shapes = {"one_block_bf16": dict(n_row=1, n_head_q=8, kv_dtype="bf16"),
               "work_group_bf16": dict(n_row=6, n_head_q=16, kv_dtype="bf16"),
-              "work_group_i8": dict(n_row=6, n_head_q=24, kv_dtype="i8")}[kind]
+              "work_group_i8": dict(n_row=6, n_head_q=24, kv_dtype="i8"),
+              "work_group_fp8": dict(n_row=6, n_head_q=24, kv_dtype="fp8")}[kind]
     wl = gen.make_decode(seed=[12, len(kind)], n_stream=2, n_head_kv=2, head_dim=128, cap=700,
                          depths=[700, 500], slice_len=256, **shapes)
     R, G = wl.n_row, wl.n_head_q // wl.n_head_kv
     k = wl.k.copy()
     ks = None if wl.k_scale is None else wl.k_scale.copy()
     for b, cell, g in [(0, 300, 1), (1, 497, 0)]:
-        if ks is not None:
-            ks[b, cell, g] = np.nan
+        if wl.kv_dtype == "i8":
+            ks[b, cell, g] = np.nan                # int8 has no NaN: a NaN row scale
+        elif wl.kv_dtype == "fp8":
+            k[b, cell, g, 5] = 0x7F                # the e4m3 NaN code
         else:
             k[b, cell, g, 5] = 0x7FC0
     wl.k, wl.k_scale = k, ks
@@ -223,7 +231,7 @@ def sel_small(seed=11, dtype="bf16", **over):
     return gen.make_prefill_sel(seed=seed, **kw)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16", "i8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "i8", "fp8"])
 def test_prefill_selection_parity(dtype):
     wl = sel_small(dtype=dtype)
     out, dev = hip_run.run_prefill(wl, dbg=True, return_dev=True)
@@ -352,7 +360,7 @@ def test_prefill_mask_control_without_nan():
     nmse_check(hip_run.run_prefill(wl), oracle_prefill(wl), TOL["f16"], "mask control")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32", "i8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "i8", "fp8"])
 def test_prefill_mask_dtypes_and_splits(dtype):
     wl = mask_small(nan=False, seed=16, kv_dtype=dtype, head_dim=256, n_row=20, n_kv=333,
                     softcap=0.0, alibi=False, excluded_rows=1)

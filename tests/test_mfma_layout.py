@@ -1,5 +1,6 @@
-"""The 16x16x32 MFMA lane layout that the matrix-core kernels rely on, checked
-on the GPU with exact small-integer inputs (one wave, fixed 64-lane buffers)."""
+"""The 16x16x32 MFMA lane layout and the e4m3 widening that the matrix-core
+kernels rely on, checked on the GPU with exact inputs (one wave, fixed 64-lane
+buffers)."""
 import ctypes
 import os
 
@@ -50,3 +51,25 @@ def test_mfma_16x16x32_layout(f16):
                           ctypes.c_void_p(d.data_ptr()), f16, ctypes.c_void_p(st)) == 0
     torch.cuda.synchronize()
     assert np.array_equal(d.cpu().numpy(), expected(a_vals, b_vals))
+
+
+def test_fp8_convert_matches_e4m3_definition():
+    """v_cvt_f32_fp8 (the e4m3 widening the kernels use for fp8 K/V) on all 256
+    codes equals the oracle's e4m3 values (TensorFold PR #911: e4m3, scale
+    amax / 448): exact for every finite code, NaN for 0x7f and 0xff."""
+    if not torch.cuda.is_available():
+        pytest.fail("needs a GPU")
+    import oracle.attention as OA
+    lib = ctypes.CDLL(LIB)
+    codes = np.arange(256, dtype=np.uint8)
+    w = torch.from_numpy(codes.view(np.int32).copy()).cuda()          # 64 words of 4 codes
+    out = torch.zeros((64, 4), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert lib.fp8_probe(ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                         ctypes.c_void_p(st)) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(256).astype(np.float64)
+    ref = OA.E4M3_TABLE
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), np.flatnonzero(np.isnan(got) != np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin]), np.flatnonzero(got[fin] != ref[fin])

@@ -329,6 +329,55 @@ def pin_storage_decoding():
     assert list(gen.f32_to_bf16_bits(x)) == [0x3F80, 0x3F82, 0x3F80]
 
 
+def pin_e4m3_decoding():
+    """e4m3 bytes (TensorFold PR #911: e4m3 rows, scale amax / 448): values that
+    follow from the format's definition, then all 256 codes against torch's
+    float8_e4m3fn decoding (a library routine)."""
+    import torch
+    t = OA.E4M3_TABLE
+    assert t[0x00] == 0.0 and t[0x80] == 0.0 and np.signbit(t[0x80])
+    assert t[0x38] == 1.0 and t[0xB8] == -1.0 and t[0x30] == 0.5 and t[0x3C] == 1.5
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x01] == 2.0 ** -9 and t[0x07] == 7 * 2.0 ** -9 and t[0x08] == 2.0 ** -6
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF]) and np.isfinite(np.delete(t, [0x7F, 0xFF])).all()
+    assert np.all(np.diff(t[:0x7F]) > 0)                     # monotone over the positive codes
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ref), np.isnan(t))
+    fin = ~np.isnan(t)
+    assert np.array_equal(ref[fin], t[fin])
+    rows = np.array([[0x38, 0xC0, 0x7E]], np.uint8)
+    assert np.array_equal(OA.kv_to_f64(rows, "fp8", np.array([0.25], np.float32)), [[0.25, -0.5, 112.0]])
+
+
+def pin_e4m3_encoding():
+    """The generator's e4m3 rounding: nearest, ties to the even code, saturating at
+    448; against torch's float -> float8_e4m3fn conversion on random values."""
+    import torch
+    # ties: 1.0625 between 0x38 and 0x39 -> 0x38; 1.1875 between 0x39 and 0x3A -> 0x3A;
+    # 2^-10 halfway between 0 and the smallest subnormal 2^-9 -> 0; 3 * 2^-11 -> 2^-9
+    x = np.array([1.0625, 1.1875, 500.0, -500.0, 2.0 ** -11, 2.0 ** -10, 3 * 2.0 ** -11, -0.0, 0.0],
+                 np.float32)
+    assert list(gen.f32_to_e4m3_bits(x)) == [0x38, 0x3A, 0x7E, 0xFE, 0x00, 0x00, 0x01, 0x00, 0x00]
+    fin = np.flatnonzero(np.isfinite(OA.E4M3_TABLE))
+    vals = OA.E4M3_TABLE[fin].astype(np.float32)
+    back = gen.f32_to_e4m3_bits(vals)
+    assert np.array_equal(OA.E4M3_TABLE[back], OA.E4M3_TABLE[fin])   # every value maps to itself
+    rng = np.random.default_rng(7)
+    r = (rng.standard_normal(20000) * rng.choice([1e-3, 1.0, 60.0], 20000)).astype(np.float32)
+    r = np.clip(r, -448, 448)
+    ref = torch.from_numpy(r).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(OA.E4M3_TABLE[gen.f32_to_e4m3_bits(r)], OA.E4M3_TABLE[ref])
+    q, sc = gen.quantize_rows_e4m3(np.array([[1.0, -3.5, 0.25], [0.0, 0.0, 0.0]], np.float32))
+    assert sc[0] == np.float32(3.5) / np.float32(448.0) and sc[1] == 0.0
+    assert q[0, 1] == 0xFE and np.all(q[1] == 0)
+    # the row quantiser (fast path) against the reference rounding, row by row
+    x = (rng.standard_normal((200, 64)) * rng.choice([1e-3, 1.0, 50.0], (200, 1))).astype(np.float32)
+    q, sc = gen.quantize_rows_e4m3(x)
+    y = (x / sc[:, None]).astype(np.float32)
+    assert np.array_equal(q, gen.f32_to_e4m3_bits(y))
+
+
 # ----------------------------------------------------------------------------
 # the scalar twin
 # ----------------------------------------------------------------------------
@@ -346,7 +395,7 @@ def _close_with_pattern(a, b, tol):
 
 
 def pin_brute_decode():
-    for i, dt in enumerate(("f32", "f16", "bf16", "i8")):
+    for i, dt in enumerate(("f32", "f16", "bf16", "i8", "fp8")):
         wl = gen.make_decode(seed=100 + i, n_stream=2, n_row=3, n_head_q=4, n_head_kv=2,
                              head_dim=4, cap=9, kv_dtype=dt, depths=[9, 2], causal=(i % 2 == 0),
                              softcap=(3.0 if i >= 2 else 0.0), alibi=(i % 2 == 1))

@@ -22,7 +22,8 @@ from typing import Optional
 
 import numpy as np
 
-KV_DTYPES = ("f32", "f16", "bf16", "i8")
+KV_DTYPES = ("f32", "f16", "bf16", "i8", "fp8")
+SCALED_DTYPES = ("i8", "fp8")        # 1-byte rows with an fp32 scale per (cell, kv head) row
 
 
 # ----------------------------------------------------------------------------
@@ -56,6 +57,43 @@ def quantize_rows_i8(x: np.ndarray):
     return q, scale
 
 
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest e4m3 value (format with maximum 448: 4 exponent bits,
+    bias 7, 3 mantissa bits, subnormals m * 2^-9), ties to the even code,
+    saturating at 448; return uint8 codes.  Inputs here are finite."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x), np.float32(448.0))
+    bits = a.view(np.uint32).astype(np.int64)
+    # normal range (>= 2^-6): keep 3 of the 23 fraction bits, round half to even on
+    # the whole bit pattern (a carry moves into the exponent), rebias 127 -> 7
+    r = (bits + 0x7FFFF + ((bits >> 20) & 1)) >> 20
+    normal = ((r >> 3) - (127 - 7)) * 8 + (r & 7)
+    # subnormal range: multiples of 2^-9, rint rounds half to even; 8 * 2^-9 is code 8
+    sub = np.rint(a.astype(np.float64) * 512.0).astype(np.int64)
+    code = np.where(a < np.float32(2.0 ** -6), sub, normal)
+    code = np.minimum(code, 0x7E).astype(np.uint8)
+    code |= np.where(np.signbit(x) & (code != 0), 0x80, 0).astype(np.uint8)
+    return code
+
+
+def quantize_rows_e4m3(x: np.ndarray):
+    """e4m3 rows with one fp32 scale per row: scale = amax / 448 in fp32, codes =
+    nearest e4m3 of x / scale (computed in fp32); an all-zero row gets scale 0.
+    The rounding runs through torch's float8_e4m3fn conversion (nearest, ties to
+    even; the values are within +-448 here), which the oracle pins check against
+    f32_to_e4m3_bits; it is the fast path for large caches."""
+    import torch
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    y = np.clip(x / safe[..., None], -448.0, 448.0).astype(np.float32)
+    q = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    q[q == 0x80] = 0                                    # -0 is stored as +0
+    q[scale == 0] = 0
+    return q, scale
+
+
 def _to_storage(x32: np.ndarray, dtype: str):
     """fp32 draw -> (storage array, scale or None)."""
     if dtype == "f32":
@@ -66,6 +104,8 @@ def _to_storage(x32: np.ndarray, dtype: str):
         return f32_to_bf16_bits(x32), None
     if dtype == "i8":
         return quantize_rows_i8(x32)
+    if dtype == "fp8":
+        return quantize_rows_e4m3(x32)
     raise ValueError(f"unknown kv dtype {dtype!r}")
 
 
@@ -180,7 +220,8 @@ class PrefillWorkload:
 
 def _draw_kv_prefix(rng, n_stream, cap, n_head_kv, head_dim, dtype, kv_len):
     """K or V for cells [0, kv_len[b]) of each stream; unused capacity is NaN
-    (int8: 0 with a NaN row scale), so a read past kv_len cannot go unnoticed."""
+    (int8: 0 with a NaN row scale; e4m3: the NaN code and a NaN scale), so a read
+    past kv_len cannot go unnoticed."""
     shape = (n_stream, cap, n_head_kv, head_dim)
     if dtype == "f32":
         store = np.full(shape, np.nan, np.float32)
@@ -188,9 +229,11 @@ def _draw_kv_prefix(rng, n_stream, cap, n_head_kv, head_dim, dtype, kv_len):
         store = np.full(shape, np.nan, np.float16)
     elif dtype == "bf16":
         store = np.full(shape, 0x7FC0, np.uint16)
+    elif dtype == "fp8":
+        store = np.full(shape, 0x7F, np.uint8)                    # the e4m3 NaN code
     else:
         store = np.zeros(shape, np.int8)
-    scales = np.full((n_stream, cap, n_head_kv), np.nan, np.float32) if dtype == "i8" else None
+    scales = np.full((n_stream, cap, n_head_kv), np.nan, np.float32) if dtype in SCALED_DTYPES else None
     for b in range(n_stream):
         n = int(kv_len[b])
         x = rng.standard_normal((n, n_head_kv, head_dim), dtype=np.float32)
@@ -273,6 +316,8 @@ def make_prefill_mask(*, seed, n_row, n_head_q, n_head_kv, head_dim, n_kv, kv_dt
         flat = k.reshape(-1)
         if kv_dtype == "bf16":
             flat[nan_idx] = np.uint16(0x7FC0)
+        elif kv_dtype == "fp8":
+            flat[nan_idx] = np.uint8(0x7F)
         else:
             flat[nan_idx] = np.nan
     if scale is None:
@@ -338,11 +383,12 @@ def config1() -> DecodeWorkload:
                        slice_len=64, scale=1.0 / 16.0, name="dense_decode_tiny")
 
 
-def config2(cap: int = 32768) -> DecodeWorkload:
-    """Split-K decode: 16 streams x 1 row, 32/4 heads, D=256, bf16, depths U[1024, 32768], slices of 1024."""
+def config2(cap: int = 32768, kv_dtype: str = "bf16") -> DecodeWorkload:
+    """Split-K decode: 16 streams x 1 row, 32/4 heads, D=256, bf16, depths U[1024, 32768], slices of 1024.
+    kv_dtype="fp8" stores the same draws as e4m3 rows with fp32 row scales."""
     return make_decode(seed=[2, 0], n_stream=16, n_row=1, n_head_q=32, n_head_kv=4,
-                       head_dim=256, cap=cap, kv_dtype="bf16", depth_range=(1024, 32768),
-                       causal=True, slice_len=1024, name="split_k_decode_bf16")
+                       head_dim=256, cap=cap, kv_dtype=kv_dtype, depth_range=(1024, 32768),
+                       causal=True, slice_len=1024, name=f"split_k_decode_{kv_dtype}")
 
 
 def config3() -> PrefillWorkload:
