@@ -12,6 +12,7 @@ Parity status of each function is stated in the header of attention.py.
 
 from .attention import (  # noqa: F401
     kv_to_f64,
+    tree_path,
     visible_decode_row,
     visible_mask_row,
     visible_selection,

@@ -28,6 +28,12 @@ Passages followed (page title; part of the page):
   is sorted, invalid and duplicate entries skipped; K/V gathered by block):
   strix-llama.cpp PR #115, "Overview" and the commit message of the Vulkan
   selected-key kernel.
+* Tree-shaped verify windows (a parent table in heap order instead of a
+  causal chain; widths 1 to 16): TensorFold PR #2595, "Kernel contract" gate
+  on tree widths and visible-key counts.
+* Attention-sink logit (a per-head logit that joins the softmax denominator;
+  -inf sink on an empty row gives 0, +inf or NaN gives NaN): HartsyInference
+  PR #910, PR body first paragraph and the review of the CPU fix.
 
 Readings where the pages are silent (each also listed in the design notes):
 * a -inf mask entry excludes the key before any arithmetic (NaN data in that
@@ -39,13 +45,25 @@ Readings where the pages are silent (each also listed in the design notes):
 * selection ids are block ids over `block_size` cells; id < 0 or
   id * block_size >= N is invalid; cells of a last partial block at or past N
   are dropped; the union over the list is a set (duplicates collapse);
-* decode row r of stream b sits at position kv_len[b] - R + r.
+* decode row r of stream b sits at position kv_len[b] - R + r;
+* tree window: the last R cells of a stream are the window's nodes in order;
+  node r's parent is parent[b][r] (heap order: parent < child; -1, or any
+  entry outside [-1, r), makes r a root hanging off the cached prefix); row r
+  sees every cell before the window plus the cells of r and its ancestors;
+  ALiBi keeps the cache slot kv_len[b] - R + r as the row's position;
+* the sink is a logit without a value: out = sum_j e^(s_j - M) v_j /
+  (sum_j e^(s_j - M) + e^(sink - M)) with M = max(max_j s_j, sink); it is
+  taken once per (row, head), after the combine of a split call, not per slice;
+  it is used as given (no scale, softcap, ALiBi or mask); the NaN / +inf /
+  -inf rules of the scores apply to it as to one more score.
 
 Parity pins (tests/test_oracle_pins.py): the printed M03 example, closed forms
 (softcap-then-ALiBi, F32 bias range, finite sentinel, one key, Q = 0, two-key
-logistic), library reductions (scipy softmax, torch CPU SDPA in float64),
-invariances (split == unsplit, list permutation / duplicates / invalid ids,
-GQA == MHA with repeated heads) and a scalar pure-Python twin (brute.py).
+logistic, one key against a sink, binary-heap ancestor counts), library
+reductions (scipy softmax, torch CPU SDPA in float64), invariances (split ==
+unsplit, list permutation / duplicates / invalid ids, GQA == MHA with repeated
+heads, chain tree == causal window, sink == one more key with a zero value),
+the sink cases the review lists, and a scalar pure-Python twin (brute.py).
 """
 
 from __future__ import annotations
@@ -108,9 +126,28 @@ def kv_to_f64(arr, dtype, scale=None):
 # visible key sets
 # ----------------------------------------------------------------------------
 
-def visible_decode_row(kv_len, n_row, r, causal):
-    """Cells row r of a decode window sees: [0, kv_len - n_row + r] or [0, kv_len)."""
+def tree_path(parent, r):
+    """Window nodes row r of a tree window sees: r, its parent, and so on up to a root.
+
+    parent[a] in [-1, a) is a's parent; any other entry ends the walk (a root)."""
+    nodes = []
+    a = int(r)
+    while a >= 0:
+        nodes.append(a)
+        up = int(parent[a])
+        a = up if -1 <= up < a else -1
+    return sorted(nodes)
+
+
+def visible_decode_row(kv_len, n_row, r, causal, parent=None):
+    """Cells row r of a decode window sees: [0, kv_len - n_row + r] or [0, kv_len);
+    with a tree parent table, the cells before the window plus r's path in it."""
     kv_len = int(kv_len)
+    if parent is not None:
+        start = kv_len - n_row
+        win = start + np.asarray(tree_path(parent, r), dtype=np.int64)
+        cells = np.concatenate([np.arange(max(0, start), dtype=np.int64), win])
+        return cells[(cells >= 0) & (cells < kv_len)]
     lim = kv_len - n_row + r + 1 if causal else kv_len
     lim = max(0, min(lim, kv_len))
     return np.arange(lim, dtype=np.int64)
@@ -170,12 +207,22 @@ def _row_max(sh):
     return float(sh.max())
 
 
-def attend_scores(s, vc):
+def _with_sink(m, z):
+    """Row maximum once the sink logit z (None = no sink) joins the scores."""
+    if z is None:
+        return m
+    if np.isnan(m) or np.isnan(z):
+        return NAN
+    return max(m, z)
+
+
+def attend_scores(s, vc, sink=None):
     """Normalised attention output for each score row.
 
-    s [nh][n], vc [n][D].  NaN anywhere in a row, or a +inf maximum, gives a
-    NaN row; an empty row or a -inf maximum gives +0.0; otherwise
-    sum_j exp(s_j - m) v_j / sum_j exp(s_j - m).
+    s [nh][n], vc [n][D], sink [nh] or None.  M = max of the row's scores and
+    its sink.  NaN anywhere in a row or in its sink, or M = +inf, gives a NaN
+    row; an empty row with no sink, or M = -inf, gives +0.0; otherwise
+    sum_j exp(s_j - M) v_j / (sum_j exp(s_j - M) + exp(sink - M)).
     """
     s = np.asarray(s, np.float64)
     vc = np.asarray(vc, np.float64)
@@ -183,14 +230,16 @@ def attend_scores(s, vc):
     d = vc.shape[1]
     out = np.zeros((nh, d), dtype=np.float64)
     for h in range(nh):
-        m = _row_max(s[h])
+        z = None if sink is None else float(np.float32(sink[h]))
+        m = _with_sink(_row_max(s[h]), z)
         if np.isnan(m) or m == INF:
             out[h] = NAN
         elif m == -INF:
             out[h] = 0.0
         else:
             p = np.exp(s[h] - m)
-            out[h] = (p @ vc) / p.sum()
+            den = p.sum() + (0.0 if z is None else np.exp(z - m))
+            out[h] = (p @ vc) / den
     return out
 
 
@@ -223,13 +272,13 @@ def partial_scores(s, vc):
     return o, m, l
 
 
-def combine_partials(o, m, l):
+def combine_partials(o, m, l, sink=None):
     """Log-sum-exp merge of split partials.
 
-    o [ns][nh][D], m [ns][nh], l [ns][nh].  M = max over slices with NaN
-    propagating; M NaN or +inf -> NaN; M = -inf -> +0.0; otherwise slices with
-    m_s = -inf are skipped and out = sum_s w_s o_s / sum_s w_s l_s with
-    w_s = exp(m_s - M).
+    o [ns][nh][D], m [ns][nh], l [ns][nh], sink [nh] or None.  M = max over
+    slices (and the sink) with NaN propagating; M NaN or +inf -> NaN; M = -inf
+    -> +0.0; otherwise slices with m_s = -inf are skipped and
+    out = sum_s w_s o_s / (sum_s w_s l_s + exp(sink - M)) with w_s = exp(m_s - M).
     """
     o = np.asarray(o, np.float64)
     m = np.asarray(m, np.float64)
@@ -238,10 +287,11 @@ def combine_partials(o, m, l):
     out = np.zeros((nh, d))
     for h in range(nh):
         mh = m[:, h]
-        if np.isnan(mh).any():
+        z = None if sink is None else float(np.float32(sink[h]))
+        if np.isnan(mh).any() or (z is not None and np.isnan(z)):
             out[h] = NAN
             continue
-        big = mh.max() if ns else -INF
+        big = _with_sink(mh.max() if ns else -INF, z)
         if big == INF:
             out[h] = NAN
             continue
@@ -256,6 +306,8 @@ def combine_partials(o, m, l):
             w = np.exp(mh[t] - big)
             num = num + w * o[t, h]
             den = den + w * l[t, h]
+        if z is not None:
+            den = den + np.exp(z - big)
         out[h] = num / den
     return out
 
@@ -264,8 +316,10 @@ def combine_partials(o, m, l):
 # decode (split-K over slices, verify windows)
 # ----------------------------------------------------------------------------
 
-def _decode_row_scores(q64, k64, b, r, g, G, n_row, kv_len, causal, scale, softcap, slopes):
-    cells = visible_decode_row(kv_len[b], n_row, r, causal)
+def _decode_row_scores(q64, k64, b, r, g, G, n_row, kv_len, causal, scale, softcap, slopes,
+                       tree_parent=None):
+    cells = visible_decode_row(kv_len[b], n_row, r, causal,
+                               None if tree_parent is None else tree_parent[b])
     pos = int(kv_len[b]) - n_row + r
     heads = slice(g * G, (g + 1) * G)
     s = scores(q64[b, r, heads], k64[cells], cells, scale=scale, softcap=softcap,
@@ -273,9 +327,16 @@ def _decode_row_scores(q64, k64, b, r, g, G, n_row, kv_len, causal, scale, softc
     return cells, s
 
 
+def _sink_args(sinks, heads):
+    return {} if sinks is None else {"sink": np.asarray(sinks)[heads]}
+
+
 def decode(*, q, k, v, kv_dtype, kv_len, causal, scale, softcap=0.0, alibi=None,
-           k_scale=None, v_scale=None):
-    """Unsplit decode output [S][R][Hq][D] in float64 (the method's plain definition)."""
+           k_scale=None, v_scale=None, tree_parent=None, sinks=None):
+    """Unsplit decode output [S][R][Hq][D] in float64 (the method's plain definition).
+
+    tree_parent [S][R] (or None): each stream's window as a tree, overriding
+    `causal`; sinks [Hq] (or None): one sink logit per query head."""
     S, R, Hq, D = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
@@ -288,13 +349,14 @@ def decode(*, q, k, v, kv_dtype, kv_len, causal, scale, softcap=0.0, alibi=None,
             v64 = kv_to_f64(v[b, :n, g], kv_dtype, None if v_scale is None else v_scale[b, :n, g])
             for r in range(R):
                 cells, s = _decode_row_scores(q64, k64, b, r, g, G, R, kv_len, causal,
-                                              scale, softcap, alibi)
-                out[b, r, g * G:(g + 1) * G] = attend_scores(s, v64[cells])
+                                              scale, softcap, alibi, tree_parent)
+                hs = slice(g * G, (g + 1) * G)
+                out[b, r, hs] = attend_scores(s, v64[cells], **_sink_args(sinks, hs))
     return out
 
 
 def decode_split(*, q, k, v, kv_dtype, kv_len, causal, scale, slice_len, softcap=0.0,
-                 alibi=None, k_scale=None, v_scale=None):
+                 alibi=None, k_scale=None, v_scale=None, tree_parent=None, sinks=None):
     """Split form: per-slice partials, then the LSE combine.
 
     Slice t covers cells [t*L, (t+1)*L); stream b has ceil(kv_len[b] / L)
@@ -321,7 +383,7 @@ def decode_split(*, q, k, v, kv_dtype, kv_len, causal, scale, slice_len, softcap
             v64 = kv_to_f64(v[b, :n, g], kv_dtype, None if v_scale is None else v_scale[b, :n, g])
             for r in range(R):
                 cells, s = _decode_row_scores(q64, k64, b, r, g, G, R, kv_len, causal,
-                                              scale, softcap, alibi)
+                                              scale, softcap, alibi, tree_parent)
                 for t in range(nsb):
                     sel = (cells >= t * L) & (cells < (t + 1) * L)
                     o_t, m_t, l_t = partial_scores(s[:, sel], v64[cells[sel]])
@@ -329,11 +391,12 @@ def decode_split(*, q, k, v, kv_dtype, kv_len, causal, scale, slice_len, softcap
                     pm[b, r, hs, t] = m_t
                     pl[b, r, hs, t] = l_t
                 out[b, r, hs] = combine_partials(po[b, r, hs, :nsb].transpose(1, 0, 2),
-                                                 pm[b, r, hs, :nsb].T, pl[b, r, hs, :nsb].T)
+                                                 pm[b, r, hs, :nsb].T, pl[b, r, hs, :nsb].T,
+                                                 **_sink_args(sinks, hs))
     return out, po, pm, pl
 
 
-def visited_decode(*, kv_len, n_row, causal, slice_len, n_head_kv):
+def visited_decode(*, kv_len, n_row, causal, slice_len, n_head_kv, tree_parent=None):
     """Per (stream, row, kv head, slice): (count, sum of cells, sum of cells^2) visited."""
     S = len(kv_len)
     L = int(slice_len)
@@ -341,7 +404,8 @@ def visited_decode(*, kv_len, n_row, causal, slice_len, n_head_kv):
     st = np.zeros((S, n_row, n_head_kv, ns, 3), dtype=np.int64)
     for b in range(S):
         for r in range(n_row):
-            cells = visible_decode_row(kv_len[b], n_row, r, causal)
+            cells = visible_decode_row(kv_len[b], n_row, r, causal,
+                                       None if tree_parent is None else tree_parent[b])
             for t in range(ns):
                 c = cells[(cells >= t * L) & (cells < (t + 1) * L)]
                 st[b, r, :, t] = (c.size, int(c.sum()), int((c * c).sum()))
@@ -360,9 +424,10 @@ def _prefill_row_cells(r, *, n_kv, q_pos, sel, block_size, mask, causal):
 
 def prefill(*, q, k, v, kv_dtype, scale, softcap=0.0, alibi=None, q_pos=None,
             sel=None, block_size=1, mask=None, causal=False, k_scale=None, v_scale=None,
-            rows=None):
+            rows=None, sinks=None):
     """Prefill output [R][Hq][D] in float64; `rows` limits the work to a subset
-    (the other rows are left NaN so that a sampled comparison cannot pass by accident)."""
+    (the other rows are left NaN so that a sampled comparison cannot pass by accident);
+    sinks [Hq] or None."""
     R, Hq, D = q.shape
     n_kv, Hkv = k.shape[0], k.shape[1]
     G = Hq // Hkv
@@ -380,13 +445,13 @@ def prefill(*, q, k, v, kv_dtype, scale, softcap=0.0, alibi=None, q_pos=None,
             vc = kv_to_f64(v[cells, g], kv_dtype, None if v_scale is None else v_scale[cells, g])
             s = scores(q64[r, hs], kc, cells, scale=scale, softcap=softcap,
                        slopes=None if alibi is None else alibi[hs], pos=pos, mask_vals=mvals)
-            out[r, hs] = attend_scores(s, vc)
+            out[r, hs] = attend_scores(s, vc, **_sink_args(sinks, hs))
     return out
 
 
 def prefill_split(*, n_splits, q, k, v, kv_dtype, scale, softcap=0.0, alibi=None,
                   q_pos=None, sel=None, block_size=1, mask=None, causal=False,
-                  k_scale=None, v_scale=None, rows=None):
+                  k_scale=None, v_scale=None, rows=None, sinks=None):
     """Split prefill: key range [0, N) cut into n_splits contiguous ranges of
     ceil(N / n_splits) cells, partials per range, LSE combine."""
     R, Hq, D = q.shape
@@ -414,7 +479,7 @@ def prefill_split(*, n_splits, q, k, v, kv_dtype, scale, softcap=0.0, alibi=None
             o = np.stack([p[0] for p in parts])
             m = np.stack([p[1] for p in parts])
             l = np.stack([p[2] for p in parts])
-            out[r, hs] = combine_partials(o, m, l)
+            out[r, hs] = combine_partials(o, m, l, **_sink_args(sinks, hs))
     return out
 
 

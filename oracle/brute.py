@@ -7,9 +7,13 @@ position order with the online-softmax recurrence of TensorFold PR #985
 ("What this changes": running max m, correction c = exp(m_old - m),
 l = l*c + p, o = o*c + p*v, o / l at the end) instead of the closed form, every
 storage value is decoded with `struct`, and visibility is decided per key from
-the rules rather than from precomputed sets.  Agreement with attention.py to
-~1e-13 pins the vectorised indexing (GQA head mapping, strides, causal limits,
-selection dedup) and the recurrence/closed-form equivalence.
+the rules rather than from precomputed sets.  Tree windows are decided from
+node paths built forward in index order (a node's path is its parent's path
+plus itself), not by walking up; the sink logit (HartsyInference PR #910) is
+fed to the recurrence as one more key whose value is zero.  Agreement with
+attention.py to ~1e-13 pins the vectorised indexing (GQA head mapping,
+strides, causal limits, tree paths, selection dedup) and the
+recurrence/closed-form equivalence.
 """
 
 from __future__ import annotations
@@ -94,14 +98,30 @@ def _score(qv, kv, scale, softcap, slope, j, pos, maskv):
     return s
 
 
+def _tree_paths(parent):
+    """paths[a] = the window nodes a sees, built in index order."""
+    paths = []
+    for a in range(len(parent)):
+        up = int(parent[a])
+        paths.append((paths[up] if 0 <= up < a else frozenset()) | {a})
+    return paths
+
+
+def _push_sink(st, sinks, h, d):
+    if sinks is not None:
+        z = struct.unpack("<f", struct.pack("<f", float(sinks[h])))[0]
+        st.push(z, [0.0] * d)
+
+
 def decode(*, q, k, v, kv_dtype, kv_len, causal, scale, softcap=0.0, alibi=None,
-           k_scale=None, v_scale=None):
+           k_scale=None, v_scale=None, tree_parent=None, sinks=None):
     S, R, Hq, D = q.shape
     cap, Hkv = k.shape[1], k.shape[2]
     G = Hq // Hkv
     out = [[[None] * Hq for _ in range(R)] for _ in range(S)]
     for b in range(S):
         n = int(kv_len[b])
+        paths = None if tree_parent is None else _tree_paths(tree_parent[b])
         for r in range(R):
             pos = n - R + r
             for h in range(Hq):
@@ -109,19 +129,25 @@ def decode(*, q, k, v, kv_dtype, kv_len, causal, scale, softcap=0.0, alibi=None,
                 qv = [float(q[b, r, h, d]) for d in range(D)]
                 st = _Online(D)
                 for j in range(cap):
-                    if j >= n or (causal and j > pos):
+                    if j >= n:
+                        continue
+                    if paths is not None:
+                        if j >= n - R and (j - (n - R)) not in paths[r]:
+                            continue
+                    elif causal and j > pos:
                         continue
                     kv = [_value(k, (b, j, g, d), kv_dtype, k_scale, (b, j, g)) for d in range(D)]
                     vv = [_value(v, (b, j, g, d), kv_dtype, v_scale, (b, j, g)) for d in range(D)]
                     s = _score(qv, kv, scale, softcap, None if alibi is None else float(alibi[h]),
                                j, pos, None)
                     st.push(s, vv)
+                _push_sink(st, sinks, h, D)
                 out[b][r][h] = st.result()
     return out
 
 
 def prefill(*, q, k, v, kv_dtype, scale, softcap=0.0, alibi=None, q_pos=None, sel=None,
-            block_size=1, mask=None, causal=False, k_scale=None, v_scale=None):
+            block_size=1, mask=None, causal=False, k_scale=None, v_scale=None, sinks=None):
     R, Hq, D = q.shape
     n_kv, Hkv = k.shape[0], k.shape[1]
     G = Hq // Hkv
@@ -151,5 +177,6 @@ def prefill(*, q, k, v, kv_dtype, scale, softcap=0.0, alibi=None, q_pos=None, se
                 s = _score(qv, kv, scale, softcap, None if alibi is None else float(alibi[h]),
                            j, pos, mv)
                 st.push(s, vv)
+            _push_sink(st, sinks, h, D)
             out[r][h] = st.result()
     return out

@@ -431,6 +431,214 @@ def pin_visited_sets():
     assert ids[0].tolist() == [1, 2] and cells[0].tolist() == [3, 4, 5, 6, 7, 8]
 
 
+# ----------------------------------------------------------------------------
+# tree-shaped verify windows (TensorFold PR #2595, "Kernel contract": widths
+# 1..16 with heap-order parents, visible keys 33, 34, 8193, 32768..32770)
+# ----------------------------------------------------------------------------
+
+def _closure_mask(parent):
+    """Row r sees window node c iff c is reachable from r by parent steps (zero or
+    more), computed as a boolean transitive closure of the parent relation."""
+    W = len(parent)
+    A = np.zeros((W, W), dtype=bool)
+    for a, up in enumerate(parent):
+        if -1 < up < a:
+            A[a, up] = True
+    reach = np.eye(W, dtype=bool)
+    for _ in range(W):
+        reach = reach | ((reach.astype(np.int64) @ A.astype(np.int64)) > 0)
+    return reach
+
+
+def pin_tree_heap_visible_counts():
+    # binary heap: node r (1-based r + 1) has ancestors (r + 1) >> k, k = 1..floor(log2(r + 1))
+    for W in (1, 2, 4, 8, 12, 16):
+        par = gen.heap_parents(W)
+        for n in (33, 34, 8193, 32768, 32769, 32770):
+            start = n - W
+            for r in range(W):
+                depth = (r + 1).bit_length() - 1
+                cells = OA.visible_decode_row(n, W, r, True, par)
+                assert cells.size == start + depth + 1, (W, n, r)
+                win = [start + ((r + 1) >> kk) - 1 for kk in range(depth, -1, -1)]
+                assert cells[start:].tolist() == win
+                assert np.array_equal(cells[:start], np.arange(start))
+
+
+def pin_tree_chain_is_causal():
+    wl = gen.make_decode(seed=71, n_stream=3, n_row=6, n_head_q=4, n_head_kv=2, head_dim=8,
+                         cap=20, kv_dtype="bf16", depths=[20, 9, 4], causal=True, alibi=True,
+                         softcap=4.0, tree="chain")
+    kw = dict(q=wl.q, k=wl.k, v=wl.v, kv_dtype="bf16", kv_len=wl.kv_len, scale=wl.scale,
+              softcap=4.0, alibi=wl.alibi)
+    causal = oracle.decode(causal=True, **kw)
+    assert np.array_equal(oracle.decode(causal=False, tree_parent=wl.tree_parent, **kw), causal)
+    # a width-1 tree is the plain single-row decode over every cell
+    one = gen.make_decode(seed=72, n_stream=2, n_row=1, n_head_q=2, n_head_kv=1, head_dim=8,
+                          cap=11, kv_dtype="f16", depths=[11, 5], causal=False, tree="heap")
+    kw1 = dict(q=one.q, k=one.k, v=one.v, kv_dtype="f16", kv_len=one.kv_len, scale=one.scale)
+    assert np.array_equal(oracle.decode(causal=True, tree_parent=one.tree_parent, **kw1),
+                          oracle.decode(causal=False, **kw1))
+
+
+def pin_tree_torch_sdpa():
+    import torch
+    rng = np.random.default_rng(73)
+    W, n, Hq, Hkv, D = 12, 40, 4, 2, 16
+    par = gen.random_parents(rng, W)
+    par[5] = 9          # not in [-1, 5): node 5 becomes a root
+    par[7] = -3         # likewise
+    wl = gen.make_decode(seed=74, n_stream=1, n_row=W, n_head_q=Hq, n_head_kv=Hkv, head_dim=D,
+                         cap=n, kv_dtype="f32", depths=[n], causal=True, tree=par)
+    out = oracle.decode(q=wl.q, k=wl.k, v=wl.v, kv_dtype="f32", kv_len=wl.kv_len, causal=True,
+                        scale=wl.scale, tree_parent=wl.tree_parent)
+    reach = _closure_mask(par)
+    bias = np.zeros((W, n))
+    bias[:, n - W:] = np.where(reach, 0.0, -np.inf)
+    q = torch.from_numpy(wl.q[0].astype(np.float64)).permute(1, 0, 2)[None]       # [1,H,W,D]
+    k = torch.from_numpy(wl.k[0].astype(np.float64)).permute(1, 0, 2)
+    v = torch.from_numpy(wl.v[0].astype(np.float64)).permute(1, 0, 2)
+    k = k.repeat_interleave(Hq // Hkv, dim=0)[None].contiguous()
+    v = v.repeat_interleave(Hq // Hkv, dim=0)[None].contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, attn_mask=torch.from_numpy(bias)[None, None], scale=wl.scale)[0]
+    assert np.allclose(out[0], ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-14)
+
+
+def pin_tree_split_and_visited():
+    wl = gen.make_decode(seed=75, n_stream=3, n_row=8, n_head_q=4, n_head_kv=2, head_dim=8,
+                         cap=30, kv_dtype="i8", depths=[30, 13, 5], causal=True, tree="random",
+                         alibi=True)
+    kw = dict(q=wl.q, k=wl.k, v=wl.v, kv_dtype="i8", kv_len=wl.kv_len, causal=True,
+              scale=wl.scale, alibi=wl.alibi, k_scale=wl.k_scale, v_scale=wl.v_scale,
+              tree_parent=wl.tree_parent)
+    ref = oracle.decode(**kw)
+    for L in (1, 3, 4, 7, 30):
+        out = oracle.decode_split(slice_len=L, **kw)[0]
+        assert np.allclose(out, ref, rtol=1e-13, atol=1e-15), L
+        st = oracle.visited_decode(kv_len=wl.kv_len, n_row=8, causal=True, slice_len=L,
+                                   n_head_kv=2, tree_parent=wl.tree_parent)
+        for b in range(3):
+            reach = _closure_mask(wl.tree_parent[b])
+            start = int(wl.kv_len[b]) - 8
+            for r in range(8):
+                cells = [j for j in range(int(wl.kv_len[b]))
+                         if j < start or (j >= start and reach[r, j - start])]
+                c = np.array(cells, np.int64)
+                assert st[b, r, 0, :, 0].sum() == c.size
+                assert st[b, r, 1, :, 1].sum() == c.sum()
+
+
+# ----------------------------------------------------------------------------
+# attention-sink logit (HartsyInference PR #910: PR body, review of the CPU fix)
+# ----------------------------------------------------------------------------
+
+def pin_sink_one_key_closed_form():
+    # one key with score a, value x, sink z: out = x / (1 + exp(z - a))
+    q = np.array([[[1.5, -0.5]]], np.float32)
+    k = np.array([[[0.75, 0.25]]], np.float32)
+    v = np.array([[[2.0, -3.0]]], np.float32)
+    a = 0.5 * (1.5 * 0.75 - 0.5 * 0.25)
+    for z in (-3.0, 0.0, 0.5, 4.0, 60.0):
+        out = oracle.prefill(q=q, k=k, v=v, kv_dtype="f32", scale=0.5,
+                             mask=np.zeros((1, 1), np.float32), sinks=np.array([z], np.float32))
+        w = 1.0 / (1.0 + math.exp(z - a))
+        assert np.allclose(out[0, 0], [2.0 * w, -3.0 * w], rtol=1e-15, atol=1e-300), z
+
+
+def pin_sink_scipy_softmax():
+    # the sink is one more logit in the softmax whose value row is zero
+    from scipy.special import softmax
+    wl = gen.make_decode(seed=76, n_stream=2, n_row=3, n_head_q=4, n_head_kv=2, head_dim=8,
+                         cap=17, kv_dtype="f16", depths=[17, 6], causal=True, sinks="draw")
+    out = oracle.decode(q=wl.q, k=wl.k, v=wl.v, kv_dtype="f16", kv_len=wl.kv_len, causal=True,
+                        scale=wl.scale, sinks=wl.sinks)
+    for b in range(2):
+        n = int(wl.kv_len[b])
+        for r in range(3):
+            lim = n - 3 + r + 1
+            for h in range(4):
+                k64 = wl.k[b, :lim, h // 2].astype(np.float64)
+                v64 = wl.v[b, :lim, h // 2].astype(np.float64)
+                s = wl.scale * (k64 @ wl.q[b, r, h].astype(np.float64))
+                w = softmax(np.append(s, float(wl.sinks[h])))[:-1]
+                assert np.allclose(out[b, r, h], w @ v64, rtol=1e-12, atol=1e-14)
+
+
+def pin_sink_review_cases():
+    D = 3
+    empty = np.zeros((1, 0))
+    none = np.zeros((0, D))
+    # an empty row: -inf sink -> +0.0; +inf or NaN sink -> NaN; a finite sink -> +0.0
+    z = OA.attend_scores(empty, none, sink=np.array([-np.inf]))
+    assert np.array_equal(z, np.zeros((1, D))) and not np.signbit(z).any()
+    assert np.isnan(OA.attend_scores(empty, none, sink=np.array([np.inf]))).all()
+    assert np.isnan(OA.attend_scores(empty, none, sink=np.array([np.nan]))).all()
+    f = OA.attend_scores(empty, none, sink=np.array([2.5]))
+    assert np.array_equal(f, np.zeros((1, D))) and not np.signbit(f).any()
+    # a -inf sink is no sink; a +inf or NaN sink poisons a non-empty row
+    s = np.array([[0.3, -1.2, 2.0]])
+    vc = np.arange(9.0).reshape(3, 3)
+    assert np.array_equal(OA.attend_scores(s, vc, sink=np.array([-np.inf])), OA.attend_scores(s, vc))
+    assert np.isnan(OA.attend_scores(s, vc, sink=np.array([np.inf]))).all()
+    assert np.isnan(OA.attend_scores(s, vc, sink=np.array([np.nan]))).all()
+    # the same through the combine of split partials
+    o = np.array([[[1.0, 2.0, 3.0]], [[0.0, 0.0, 0.0]]])
+    m = np.array([[0.5], [-np.inf]])
+    l = np.array([[2.0], [0.0]])
+    w = 2.0 / (2.0 + math.exp(1.0 - 0.5))
+    assert np.allclose(OA.combine_partials(o, m, l, sink=np.array([1.0])),
+                       [[0.5 * w, 1.0 * w, 1.5 * w]], rtol=1e-15)
+    assert np.array_equal(OA.combine_partials(o, m, l, sink=np.array([-np.inf])),
+                          OA.combine_partials(o, m, l))
+    m_empty = np.array([[-np.inf], [-np.inf]])
+    for zz, nan in ((-np.inf, False), (np.inf, True), (np.nan, True), (0.0, False)):
+        c = OA.combine_partials(np.zeros_like(o), m_empty, np.zeros_like(l), sink=np.array([zz]))
+        if nan:
+            assert np.isnan(c).all(), zz
+        else:
+            assert np.array_equal(c, np.zeros((1, D))) and not np.signbit(c).any(), zz
+
+
+def pin_sink_split_equals_unsplit():
+    wl = gen.make_decode(seed=77, n_stream=2, n_row=4, n_head_q=4, n_head_kv=2, head_dim=8,
+                         cap=19, kv_dtype="bf16", depths=[19, 7], causal=True, sinks="draw",
+                         tree="heap")
+    kw = dict(q=wl.q, k=wl.k, v=wl.v, kv_dtype="bf16", kv_len=wl.kv_len, causal=True,
+              scale=wl.scale, sinks=wl.sinks, tree_parent=wl.tree_parent)
+    ref = oracle.decode(**kw)
+    for L in (1, 2, 5, 19):
+        assert np.allclose(oracle.decode_split(slice_len=L, **kw)[0], ref, rtol=1e-13, atol=1e-15)
+    pw = gen.make_prefill_sel(seed=78, n_row=3, n_head_q=4, n_head_kv=2, head_dim=8, n_kv=30,
+                              kv_dtype="bf16", n_sel=7, n_dup=1, n_invalid=1, block_size=3)
+    sinks = gen.draw_sinks(np.random.default_rng(79), 4)
+    kwp = dict(q=pw.q, k=pw.k, v=pw.v, kv_dtype="bf16", scale=pw.scale, q_pos=pw.q_pos,
+               sel=pw.sel, block_size=3, sinks=sinks)
+    ref = oracle.prefill(**kwp)
+    for n in (1, 2, 4, 30):
+        assert np.allclose(oracle.prefill_split(n_splits=n, **kwp), ref, rtol=1e-13, atol=1e-15)
+
+
+def pin_brute_tree_sink():
+    for i, dt in enumerate(("f32", "bf16", "i8", "fp8")):
+        wl = gen.make_decode(seed=130 + i, n_stream=2, n_row=5, n_head_q=4, n_head_kv=2,
+                             head_dim=4, cap=9, kv_dtype=dt, depths=[9, 3], causal=True,
+                             alibi=(i % 2 == 1), tree="random", sinks="draw")
+        sinks = wl.sinks.copy()
+        if i == 3:
+            sinks[1], sinks[2] = -np.inf, np.nan
+        kw = dict(q=wl.q, k=wl.k, v=wl.v, kv_dtype=dt, kv_len=wl.kv_len, causal=True,
+                  scale=wl.scale, alibi=wl.alibi, k_scale=wl.k_scale, v_scale=wl.v_scale,
+                  tree_parent=wl.tree_parent, sinks=sinks)
+        _close_with_pattern(oracle.decode(**kw), brute.decode(**kw), 1e-13)
+    wl = gen.make_prefill_mask(seed=134, n_row=4, n_head_q=4, n_head_kv=2, head_dim=4, n_kv=9,
+                               kv_dtype="f16", excluded_rows=1, softcap=20.0, alibi=True)
+    sinks = np.array([0.5, -np.inf, np.inf, 3.0], np.float32)
+    kw = dict(q=wl.q, k=wl.k, v=wl.v, kv_dtype="f16", scale=wl.scale, softcap=20.0,
+              alibi=wl.alibi, q_pos=wl.q_pos, mask=wl.mask, causal=True, sinks=sinks)
+    _close_with_pattern(oracle.prefill(**kw), brute.prefill(**kw), 1e-13)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -470,9 +678,9 @@ def test_planted_alibi_before_softcap(monkeypatch):
 def test_planted_combine_nan_to_zero(monkeypatch):
     real = OA.combine_partials
 
-    def lossy(o, m, l):
+    def lossy(o, m, l, **kw):
         m = np.nan_to_num(np.asarray(m, np.float64), nan=-np.inf)
-        return np.nan_to_num(real(o, m, l), nan=0.0)
+        return np.nan_to_num(real(o, m, l, **kw), nan=0.0)
 
     monkeypatch.setattr(OA, "combine_partials", lossy)
     _expect_red(pin_combine_rules)
@@ -493,8 +701,8 @@ def test_planted_no_dedup(monkeypatch):
 def test_planted_excluded_row_nan(monkeypatch):
     real = OA.attend_scores
 
-    def nan_rows(s, vc):
-        out = real(s, vc)
+    def nan_rows(s, vc, **kw):
+        out = real(s, vc, **kw)
         s = np.asarray(s)
         for h in range(s.shape[0]):
             if s.shape[1] == 0 or np.all(s[h] == -np.inf):
@@ -531,3 +739,54 @@ def test_planted_dropped_scale(monkeypatch):
 
     monkeypatch.setattr(OA, "scores", unscaled)
     _expect_red(pin_torch_sdpa_mask_alibi_gqa)
+
+
+def test_planted_tree_sibling_visible(monkeypatch):
+    # planted: a row also sees the node just before it (a chain step mixed into the tree)
+    real = OA.tree_path
+
+    def leaky(parent, r):
+        nodes = set(real(parent, r))
+        if r > 0:
+            nodes.add(r - 1)
+        return sorted(nodes)
+
+    monkeypatch.setattr(OA, "tree_path", leaky)
+    _expect_red(pin_tree_heap_visible_counts)
+    _expect_red(pin_tree_torch_sdpa)
+
+
+def test_planted_sink_counted_twice(monkeypatch):
+    # planted: the sink enters each slice's partial as well as the final combine
+    real = OA.combine_partials
+
+    def twice(o, m, l, sink=None):
+        if sink is None:
+            return real(o, m, l)
+        m = np.asarray(m, np.float64)
+        l2 = np.array(l, np.float64)
+        for t in range(m.shape[0]):
+            for h in range(m.shape[1]):
+                if np.isfinite(m[t, h]):
+                    l2[t, h] += math.exp(float(sink[h]) - m[t, h])
+        return real(o, m, l2, sink=sink)
+
+    monkeypatch.setattr(OA, "combine_partials", twice)
+    _expect_red(pin_sink_split_equals_unsplit)
+
+
+def test_planted_sink_guard_missing(monkeypatch):
+    # planted: no guard for M = -inf, so a -inf sink on an empty row computes exp(-inf - -inf)
+    real = OA.attend_scores
+
+    def unguarded(s, vc, sink=None):
+        s = np.asarray(s, np.float64)
+        if sink is not None and s.shape[1] == 0:
+            z = np.asarray(sink, np.float64)
+            with np.errstate(invalid="ignore"):
+                den = np.exp(z - np.maximum(z, -np.inf))
+            return np.zeros((s.shape[0], np.asarray(vc).shape[1])) / den[:, None]
+        return real(s, vc, sink=sink)
+
+    monkeypatch.setattr(OA, "attend_scores", unguarded)
+    _expect_red(pin_sink_review_cases)

@@ -148,6 +148,8 @@ class DecodeWorkload:
     kv_len int32 [S]: cells in each stream's cache, the window's rows included
     Row r of stream b sits at position kv_len[b] - R + r; with causal it sees
     cells [0, that position], else [0, kv_len[b]).
+    tree_parent int32 [S][R] or None: each stream's window as a tree in heap order
+    sinks fp32 [Hq] or None: one sink logit per query head
     """
 
     name: str
@@ -169,6 +171,8 @@ class DecodeWorkload:
     softcap: float
     alibi: Optional[np.ndarray]
     slice_len: int
+    tree_parent: Optional[np.ndarray] = None
+    sinks: Optional[np.ndarray] = None
     meta: dict = field(default_factory=dict)
 
     @property
@@ -185,6 +189,7 @@ class PrefillWorkload:
     q_pos  int32 [R] query positions (ALiBi and causal)
     Selection mode: sel int32 [R][n_sel] block ids, block_size cells per id.
     Mask mode: mask fp32 [R][N] additive (broadcast over heads), causal flag.
+    sinks  fp32 [Hq] or None: one sink logit per query head
     """
 
     name: str
@@ -207,6 +212,7 @@ class PrefillWorkload:
     block_size: int = 1
     mask: Optional[np.ndarray] = None
     causal: bool = False
+    sinks: Optional[np.ndarray] = None
     meta: dict = field(default_factory=dict)
 
     @property
@@ -217,6 +223,32 @@ class PrefillWorkload:
 # ----------------------------------------------------------------------------
 # generic builders (tests use them at small sizes)
 # ----------------------------------------------------------------------------
+
+def heap_parents(width: int) -> np.ndarray:
+    """Binary tree in heap order: node i > 0 hangs off node (i - 1) // 2, node 0 is the root."""
+    return np.array([-1] + [(i - 1) // 2 for i in range(1, width)], dtype=np.int32)
+
+
+def chain_parents(width: int) -> np.ndarray:
+    """A chain: node i hangs off node i - 1 (the causal window as a tree)."""
+    return np.arange(-1, width - 1, dtype=np.int32)
+
+
+def random_parents(rng, width: int) -> np.ndarray:
+    """Random tree in heap order: node i's parent uniform over {-1, 0, ..., i - 1}."""
+    return np.array([int(rng.integers(-1, i)) for i in range(width)], dtype=np.int32)
+
+
+def aux_rng(seed):
+    """A generator independent of the main draw of `seed` (trees, sinks), so that
+    adding them leaves Q, K, V and the lengths unchanged."""
+    return np.random.default_rng(np.random.SeedSequence(seed).spawn(1)[0])
+
+
+def draw_sinks(rng, n_head: int) -> np.ndarray:
+    """Sink logits U[-2, 6): from below the typical score maximum to well above it."""
+    return rng.uniform(-2.0, 6.0, size=n_head).astype(np.float32)
+
 
 def _draw_kv_prefix(rng, n_stream, cap, n_head_kv, head_dim, dtype, kv_len):
     """K or V for cells [0, kv_len[b]) of each stream; unused capacity is NaN
@@ -246,13 +278,16 @@ def _draw_kv_prefix(rng, n_stream, cap, n_head_kv, head_dim, dtype, kv_len):
 
 def make_decode(*, seed, n_stream, n_row, n_head_q, n_head_kv, head_dim, cap,
                 kv_dtype, depths=None, depth_range=None, causal=True,
-                slice_len=1024, scale=None, softcap=0.0, alibi=False,
-                name="decode") -> DecodeWorkload:
+                slice_len=1024, scale=None, softcap=0.0, alibi=False, tree=None,
+                sinks=None, name="decode") -> DecodeWorkload:
     """Decode workload.
 
     With fixed `depths`: Q, K, V ~ N(0,1) over the whole capacity, in that order.
     With `depth_range`: Q, then the depths U[lo, hi] (inclusive), then K and V
     for the cells below each depth only (unused capacity holds NaN).
+    tree: None, "heap", "chain", "random" (one random tree per stream) or an
+    int array [R] used by every stream.  sinks: None, "draw" or an array [Hq].
+    Trees and sinks come from aux_rng(seed).
     """
     assert kv_dtype in KV_DTYPES
     rng = np.random.default_rng(seed)
@@ -269,9 +304,23 @@ def make_decode(*, seed, n_stream, n_row, n_head_q, n_head_kv, head_dim, cap,
     if scale is None:
         scale = 1.0 / np.sqrt(head_dim)
     slopes = alibi_slopes(n_head_q) if alibi else None
+    aux = aux_rng(seed)
+    parents = None
+    if isinstance(tree, str) and tree == "random":
+        parents = np.stack([random_parents(aux, n_row) for _ in range(n_stream)])
+    elif tree is not None:
+        one = {"heap": heap_parents, "chain": chain_parents}[tree](n_row) if isinstance(tree, str) \
+            else np.asarray(tree, np.int32)
+        parents = np.tile(one, (n_stream, 1)).astype(np.int32)
+    sk = None
+    if isinstance(sinks, str):
+        sk = draw_sinks(aux, n_head_q)
+    elif sinks is not None:
+        sk = np.asarray(sinks, np.float32)
     return DecodeWorkload(name, n_stream, n_row, n_head_q, n_head_kv, head_dim, cap,
                           kv_dtype, q, k, v, ks, vs, kv_len, bool(causal), float(scale),
-                          float(softcap), slopes, int(slice_len))
+                          float(softcap), slopes, int(slice_len), tree_parent=parents,
+                          sinks=sk)
 
 
 def make_prefill_mask(*, seed, n_row, n_head_q, n_head_kv, head_dim, n_kv, kv_dtype,
