@@ -276,6 +276,27 @@ def main():
                                    "ms": round(ms5, 5), "gbs": round(bytes5 / (ms5 * 1e-3) / 1e9, 2),
                                    "tflops": round(flops5 / (ms5 * 1e-3) / 1e12, 2)}
         del d5
+        log("generating the int8 tree verify-window workload")
+        wl5t = gen.config5(32000, tree="heap")
+        d5t = hip_run.DecodeDev(wl5t, "cuda", poison_outputs=False)
+        a5t, c5t = d5t.args(), d5t.combine_args()
+
+        def step5t():
+            sa.sel_attn_decode(a5t)
+            sa.sel_attn_split_combine(c5t)
+
+        step5t()
+        ms5t = timed(step5t, args.steps, torch)
+        # visible keys of heap node r: the cached prefix plus floor(log2(r + 1)) + 1 window nodes
+        flops5t = 0.0
+        for r in range(wl5t.n_row):
+            vis = int(wl5t.kv_len[0]) - wl5t.n_row + (r + 1).bit_length()
+            flops5t += 4.0 * wl5t.head_dim * wl5t.n_head_q * wl5t.n_stream * vis
+        result["tree_verify_decode"] = {"workload": "int8 verify as above, each window a 16-node binary "
+                                                    "tree in heap order",
+                                        "ms": round(ms5t, 5), "gbs": round(bytes5 / (ms5t * 1e-3) / 1e9, 2),
+                                        "tflops": round(flops5t / (ms5t * 1e-3) / 1e12, 2)}
+        del d5t
         log("generating the split-K decode workload with e4m3 K/V")
         wl2f = gen.config2(kv_dtype="fp8")
         d2f = hip_run.DecodeDev(wl2f, "cuda", poison_outputs=False)

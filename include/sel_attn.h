@@ -23,12 +23,17 @@
  *   if softcap > 0:  s_j = softcap * tanh(s_j / softcap)      (softcap first ...)
  *   if alibi:        s_j += slope[h] * (j - pos)              (... then ALiBi ...)
  *   if mask:         s_j += mask[row][j]   (F32, never clamped; added last)
- *   out = sum_j exp(s_j - m) v_j / sum_j exp(s_j - m) over the visible keys.
+ *   out = sum_j exp(s_j - m) v_j / (sum_j exp(s_j - m) + exp(sink_h - m))
+ *         over the visible keys, m = max(max_j s_j, sink_h); without sinks the
+ *         sink term is absent (the same as sink_h = -inf).
  *   - a key outside the visible set is never read (NaN stored there has no
  *     effect); a -inf mask entry removes the key from the visible set;
  *   - an empty visible set, or one whose scores are all -inf, gives +0.0;
  *   - any NaN score in the visible set, or a +inf maximum, gives NaN in every
- *     output dim of that (row, head); NaN in v_j at dim d gives NaN at dim d.
+ *     output dim of that (row, head); NaN in v_j at dim d gives NaN at dim d;
+ *   - the sink counts as one more score for these rules: a NaN or +inf sink
+ *     gives NaN, a -inf sink changes nothing, and an empty row gives +0.0 with
+ *     any other sink.
  *   Query head h reads kv head h / (n_head_q / n_head_kv).
  *   Accumulation is fp32; bf16/fp16/int8 paths round Q (and the softmax
  *   weights before the P.V product) to bf16 or fp16 for the matrix cores.
@@ -39,9 +44,11 @@
  *                                          "Kernel contract";
  *   maskless selected-key attention ...... strix-llama.cpp PR #115, "Overview"
  *                                          and the Vulkan selected-key commit message;
- *   softcap/ALiBi order, F32 mask, zero rows, NaN through the combine
- *                                          ... HartsyInference PR #910, PR body,
- *                                          review and the M03 follow-up comment.
+ *   softcap/ALiBi order, F32 mask, zero rows, NaN through the combine,
+ *   attention-sink logit ................. HartsyInference PR #910, PR body,
+ *                                          review and the M03 follow-up comment;
+ *   tree-shaped verify windows ........... TensorFold PR #2595, "Kernel contract"
+ *                                          (tree widths with heap-order parents).
  */
 #ifndef SEL_ATTN_H
 #define SEL_ATTN_H
@@ -53,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SEL_ATTN_ABI_VERSION 1
+#define SEL_ATTN_ABI_VERSION 2
 
 /* status codes */
 #define SEL_ATTN_OK            0
@@ -82,7 +89,17 @@ extern "C" {
  * Stream b holds kv_len[b] cells (clamped to [0, cap]); its n_row query rows
  * are the newest rows of that cache: row r sits at position
  * pos = kv_len[b] - n_row + r and sees cells [0, pos] when `causal`, else
- * [0, kv_len[b]).  ALiBi uses (j - pos).  Slice t covers cells
+ * [0, kv_len[b]).  ALiBi uses (j - pos).
+ *
+ * Tree windows (tree_parent != NULL; TensorFold PR #2595: tree widths 1..16
+ * with heap-order parents): the window cells kv_len[b] - n_row + a, a in
+ * [0, n_row), are the nodes of a tree; tree_parent[b*n_row + a] is the parent
+ * of node a, which must precede it (-1 or any entry outside [-1, a) makes a a
+ * root).  Row r then sees every cell before the window plus the window cells
+ * of r and its ancestors; `causal` is ignored and pos is as above.  n_row must
+ * be at most 64 (else EUNSUPPORTED).  The table is read on the device.
+ *
+ * Slice t covers cells
  * [t*slice_len, (t+1)*slice_len); a stream has ceil(kv_len[b] / slice_len)
  * slices and the kernel writes, for every one of them and every (row, head),
  * an unnormalised partial:
@@ -127,6 +144,7 @@ typedef struct sel_attn_decode_args {
     int64_t* dbg_visit;          /* NULL, or [S][R][Hkv][n_slices_max][3]: for each
                                     slice the kernel ran, {count, sum cell, sum cell^2}
                                     of the cells it combined for that row */
+    const int32_t* tree_parent;  /* NULL, or [S][R] device: tree windows (above) */
 } sel_attn_decode_args;
 
 /*
@@ -135,7 +153,10 @@ typedef struct sel_attn_decode_args {
  * PR #910 review item 1).  For each (b, r, h): M = max over the stream's slices
  * of m (NaN if any is NaN); M NaN or +inf -> NaN output; M = -inf -> +0.0;
  * else out = sum_t w_t o_t / sum_t w_t l_t with w_t = exp(m_t - M), slices
- * with m_t = -inf skipped.
+ * with m_t = -inf skipped.  With sinks (fp32 [Hq] device, one logit per query
+ * head; HartsyInference PR #910) M also takes sinks[h] and the denominator
+ * gains exp(sinks[h] - M); a NaN sink gives NaN.  The sink is applied here
+ * only, once per (b, r, h): decode partials never hold it.
  * Slice count of stream b: ceil(min(max(kv_len[b], 0), cap) / slice_len) when
  * kv_len is given, else n_slices_max for every stream.
  * out fp32 [S][R][Hq][D] contiguous.  EINVAL: null part_o/part_ml/out,
@@ -152,6 +173,7 @@ typedef struct sel_attn_combine_args {
     const float* part_o;
     const float* part_ml;
     float* out;
+    const float* sinks;          /* [Hq] device, or NULL */
 } sel_attn_combine_args;
 
 /*
@@ -172,11 +194,13 @@ typedef struct sel_attn_combine_args {
  * g*kv_stride_head + d, int8 scales at cell*sc_stride_cell + g*sc_stride_head.
  * q_pos int32 [R] is required when causal or ALiBi is used.
  *
- * n_splits == 1: out fp32 [R][Hq][D].  n_splits > 1: the key range [0, n_kv)
+ * n_splits == 1: out fp32 [R][Hq][D], with the sink logits `sinks` (fp32 [Hq]
+ * device, or NULL) in the softmax.  n_splits > 1: the key range [0, n_kv)
  * is cut into n_splits ranges of ceil(n_kv / n_splits) cells and partials in
  * the decode format are written to part_o [R][Hq][n_splits][D] and
- * part_ml [R][Hq][n_splits][2]; sel_attn_split_combine with n_stream = 1,
- * n_slices_max = n_splits and kv_len = NULL merges them.
+ * part_ml [R][Hq][n_splits][2] (`sinks` is not read); sel_attn_split_combine
+ * with n_stream = 1, n_slices_max = n_splits, kv_len = NULL and the sinks
+ * merges them.
  *
  * Debug outputs (NULL to skip): dbg_visit int64 [R][Hkv][n_splits][3]
  * {count, sum cell, sum cell^2} of the cells combined; dbg_sel int32
@@ -219,6 +243,7 @@ typedef struct sel_attn_prefill_args {
     float* part_ml;
     int64_t* dbg_visit;
     int32_t* dbg_sel;
+    const float* sinks;          /* [Hq] device, or NULL (n_splits == 1 only) */
 } sel_attn_prefill_args;
 
 /* Entry points.  Return SEL_ATTN_OK or a negative status; see above. */

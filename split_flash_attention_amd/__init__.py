@@ -32,7 +32,7 @@ class DecodeArgs(ctypes.Structure):
         ("sc_stride_stream", _i64), ("sc_stride_cell", _i64), ("sc_stride_head", _i64),
         ("kv_len", _p), ("causal", _i32), ("scale", _f32), ("softcap", _f32),
         ("alibi_slopes", _p), ("slice_len", _i32), ("n_slices_max", _i32),
-        ("part_o", _p), ("part_ml", _p), ("dbg_visit", _p),
+        ("part_o", _p), ("part_ml", _p), ("dbg_visit", _p), ("tree_parent", _p),
     ]
 
 
@@ -40,7 +40,7 @@ class CombineArgs(ctypes.Structure):
     _fields_ = [
         ("n_stream", _i32), ("n_row", _i32), ("n_head_q", _i32), ("head_dim", _i32),
         ("n_slices_max", _i32), ("kv_len", _p), ("slice_len", _i32), ("cap", _i32),
-        ("part_o", _p), ("part_ml", _p), ("out", _p),
+        ("part_o", _p), ("part_ml", _p), ("out", _p), ("sinks", _p),
     ]
 
 
@@ -54,7 +54,7 @@ class PrefillArgs(ctypes.Structure):
         ("sel", _p), ("n_sel", _i32), ("block_size", _i32),
         ("mask", _p), ("mask_stride_row", _i64), ("mask_stride_head", _i64), ("causal", _i32),
         ("n_splits", _i32), ("out", _p), ("part_o", _p), ("part_ml", _p),
-        ("dbg_visit", _p), ("dbg_sel", _p),
+        ("dbg_visit", _p), ("dbg_sel", _p), ("sinks", _p),
     ]
 
 
@@ -132,10 +132,11 @@ def kv_dtype_code(t) -> int:
 
 
 def decode_args(*, q, k, v, kv_len, part_o, part_ml, causal=True, scale, softcap=0.0,
-                alibi=None, slice_len, k_scale=None, v_scale=None, dbg_visit=None) -> DecodeArgs:
+                alibi=None, slice_len, k_scale=None, v_scale=None, dbg_visit=None,
+                tree_parent=None) -> DecodeArgs:
     """Fill the decode struct from tensors: q [S][R][Hq][D] fp32 contiguous,
     k/v [S][cap][Hkv][D] (dim contiguous), scales [S][cap][Hkv], kv_len int32 [S],
-    part_o [S][R][Hq][ns][D], part_ml [S][R][Hq][ns][2]."""
+    part_o [S][R][Hq][ns][D], part_ml [S][R][Hq][ns][2], tree_parent int32 [S][R]."""
     S, R, Hq, D = q.shape
     a = DecodeArgs()
     a.n_stream, a.n_row, a.n_head_q, a.head_dim = S, R, Hq, D
@@ -154,6 +155,7 @@ def decode_args(*, q, k, v, kv_len, part_o, part_ml, causal=True, scale, softcap
     a.slice_len = int(slice_len)
     a.n_slices_max = part_o.shape[3]
     a.part_o, a.part_ml, a.dbg_visit = _ptr(part_o), _ptr(part_ml), _ptr(dbg_visit)
+    a.tree_parent = _ptr(tree_parent)
     return a
 
 
@@ -161,13 +163,16 @@ def sel_attn_decode(args: DecodeArgs, stream=None):
     _check(lib().sel_attn_decode(ctypes.byref(args), _stream(stream)), "sel_attn_decode")
 
 
-def combine_args(*, part_o, part_ml, out, kv_len=None, slice_len=0, cap=0) -> CombineArgs:
+def combine_args(*, part_o, part_ml, out, kv_len=None, slice_len=0, cap=0,
+                 sinks=None) -> CombineArgs:
+    """part_o [S][R][Hq][ns][D], part_ml [S][R][Hq][ns][2], out [S][R][Hq][D], sinks fp32 [Hq]."""
     S, R, Hq, ns, D = part_o.shape
     a = CombineArgs()
     a.n_stream, a.n_row, a.n_head_q, a.head_dim, a.n_slices_max = S, R, Hq, D, ns
     a.kv_len = _ptr(kv_len)
     a.slice_len, a.cap = int(slice_len), int(cap)
     a.part_o, a.part_ml, a.out = _ptr(part_o), _ptr(part_ml), _ptr(out)
+    a.sinks = _ptr(sinks)
     return a
 
 
@@ -178,9 +183,10 @@ def sel_attn_split_combine(args: CombineArgs, stream=None):
 def prefill_args(*, q, k, v, out=None, scale, softcap=0.0, alibi=None, q_pos=None, sel=None,
                  block_size=1, mask=None, mask_stride_head=0, causal=False, k_scale=None,
                  v_scale=None, n_splits=1, part_o=None, part_ml=None, dbg_visit=None,
-                 dbg_sel=None) -> PrefillArgs:
+                 dbg_sel=None, sinks=None) -> PrefillArgs:
     """q [R][Hq][D] fp32; k/v [N][Hkv][D]; sel int32 [R][n_sel] or mask fp32 [R][N]
-    (row stride taken from the tensor, head stride as given, 0 = broadcast)."""
+    (row stride taken from the tensor, head stride as given, 0 = broadcast);
+    sinks fp32 [Hq] (read when n_splits == 1)."""
     R, Hq, D = q.shape
     a = PrefillArgs()
     a.n_row, a.n_head_q, a.head_dim = R, Hq, D
@@ -203,6 +209,7 @@ def prefill_args(*, q, k, v, out=None, scale, softcap=0.0, alibi=None, q_pos=Non
     a.n_splits = int(n_splits)
     a.out, a.part_o, a.part_ml = _ptr(out), _ptr(part_o), _ptr(part_ml)
     a.dbg_visit, a.dbg_sel = _ptr(dbg_visit), _ptr(dbg_sel)
+    a.sinks = _ptr(sinks)
     return a
 
 

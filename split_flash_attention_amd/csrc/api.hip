@@ -63,6 +63,7 @@ int validate_decode(const sel_attn_decode_args* a) {
     if (!aligned16(a->q) || !aligned16(a->part_o)) return SEL_ATTN_EUNSUPPORTED;
     if (static_cast<int64_t>(a->n_slices_max) * a->slice_len < a->cap) return SEL_ATTN_EWORKSPACE;
     if (static_cast<int64_t>(a->n_stream) * a->n_slices_max > 0x7fffffffLL) return SEL_ATTN_EUNSUPPORTED;
+    if (a->tree_parent && a->n_row > 64) return SEL_ATTN_EUNSUPPORTED;   // one 64-bit path mask per row
     return SEL_ATTN_OK;
 }
 

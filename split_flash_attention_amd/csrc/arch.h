@@ -49,6 +49,13 @@ __device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
 __device__ __forceinline__ float wave_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
 __device__ __forceinline__ int wave_xor_i(int x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// Lane `src`'s 64-bit value (two 32-bit exchanges).
+__device__ __forceinline__ unsigned long long wave_read64(unsigned long long x, int src) {
+    const unsigned lo = static_cast<unsigned>(__shfl(static_cast<int>(x & 0xffffffffull), src, 64));
+    const unsigned hi = static_cast<unsigned>(__shfl(static_cast<int>(x >> 32), src, 64));
+    return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
 // Wave-uniform "does any lane hold true".
 __device__ __forceinline__ bool wave_any(bool x) { return __any(x); }
 

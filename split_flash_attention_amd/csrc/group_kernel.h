@@ -28,7 +28,7 @@ namespace mk {
 // query vectors x D, bf16/fp16, in operand order) and its visit counters.
 template <int D, int W>
 constexpr int group_smem() {
-    return kTK * D * 2 + D * 64 + 2 * kTK * 4 + W * D * 32 + W * 16 * 3 * 8;
+    return kTK * D * 2 + D * 64 + 2 * kTK * 4 + W * D * 32 + W * 16 * 3 * 8 + W * 16 * 8;
 }
 
 template <int KT, int D, int W>
@@ -55,6 +55,7 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     char* q_lds = reinterpret_cast<char*>(vsc_lds + kTK);          // W * D * 32
     unsigned long long* dbg_lds =                                  // W * 16 * 3
         reinterpret_cast<unsigned long long*>(q_lds + W * D * 32);
+    unsigned long long* tpath_lds = dbg_lds + W * 16 * 3;          // W * 16
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -82,8 +83,16 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     ok = ok && r < p.R;
     if (!ok) { r = 0; h = g * G; }
     const int pos = kvl - p.R + r;
-    int lim = min(p.causal ? min(pos + 1, kvl) : kvl, hi);
+    const bool tree = p.tree != nullptr;
+    int lim = min((p.causal && !tree) ? min(pos + 1, kvl) : kvl, hi);
     if (!ok) lim = -1;
+    // tree windows: the window nodes this query vector sees, kept in LDS for the
+    // partial tiles (read after the first tile's barrier)
+    unsigned long long* my_tpath = tpath_lds + wave * 16 + ln;
+    if (tree) {                                 // uniform
+        const unsigned long long path = tree_path_mask_wave(p.tree + static_cast<int64_t>(b) * p.R, p.R, r);
+        if (lg == 0) *my_tpath = path;
+    }
 
     // Q^T operands, scale folded in, kept in this wave's part of LDS (registers go
     // to the O^T accumulators): step kk of lane l at kk * 1024 + l * 16
@@ -114,9 +123,9 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     // (lim_max); keys below lim_min are seen by every query vector of it
     int lim_max = -1, lim_min = 0x7fffffff;
     for (int rr = m_wg / G; rr <= (m_end - 1) / G && rr < p.R; ++rr) {
-        const int l = p.causal ? min(kvl - p.R + rr + 1, kvl) : kvl;
+        const int l = (p.causal && !tree) ? min(kvl - p.R + rr + 1, kvl) : kvl;
         lim_max = max(lim_max, l);
-        lim_min = min(lim_min, l);
+        lim_min = min(lim_min, tree ? max(kvl - p.R, 0) : l);
     }
     const int n_keys = max(0, min(hi, lim_max) - lo);
     const int n_full = max(0, min(hi, lim_min) - lo);      // key slots visible to all
@@ -316,20 +325,34 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         // maximum (v_max_f32 returns the other operand) and shows up as a NaN weight,
         // hence a NaN running sum, which the epilogue turns into the NaN flag.
         const bool full = t0 + kTK <= n_full;
-        const int vlim = lim - cell0;               // partial tile: visible iff off(e) < vlim
+        // partial tile: bit o of vword says whether key slot o (cell cell0 + o) is visible
+        uint32_t vword;
+        {
+            const int vlim = lim - cell0;
+            vword = vlim >= 32 ? 0xffffffffu : (vlim <= 0 ? 0u : (1u << vlim) - 1u);
+            if (tree) {                             // uniform: window cells by path mask
+                const unsigned long long path = *my_tpath;
+                const int w0 = kvl - p.R - cell0;   // slot of the window's first node
+                uint32_t keep;
+                if (w0 >= 32) keep = 0xffffffffu;
+                else if (w0 >= 0) keep = ((1u << w0) - 1u) | static_cast<uint32_t>(path << w0);
+                else keep = w0 <= -64 ? 0u : static_cast<uint32_t>(path >> (-w0));
+                vword &= keep;
+            }
+        }
         float tmax = kNegInf;
         if (full) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, sc[e]);
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, (e >> 2) * 16 + (e & 3) < vlim ? sc[e] : kNegInf);
+            for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, ((vword >> ((e >> 2) * 16 + (e & 3))) & 1u) ? sc[e] : kNegInf);
         }
         if (p.dbg_visit) {
             unsigned long long c = 0, sm = 0, sq = 0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                if (full || (e >> 2) * 16 + (e & 3) < vlim) {
+                if (full || ((vword >> ((e >> 2) * 16 + (e & 3))) & 1u)) {
                     const unsigned long long cell = cell0 + (e >> 2) * 16 + (e & 3);
                     c += 1;
                     sm += cell;
@@ -360,7 +383,7 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                pv[e] = (e >> 2) * 16 + (e & 3) < vlim ? __builtin_amdgcn_exp2f(fmaf(sc[e], kLog2e, -mls)) : 0.f;
+                pv[e] = ((vword >> ((e >> 2) * 16 + (e & 3))) & 1u) ? __builtin_amdgcn_exp2f(fmaf(sc[e], kLog2e, -mls)) : 0.f;
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) l_run += pv[e];

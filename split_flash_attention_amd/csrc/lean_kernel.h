@@ -39,7 +39,7 @@ __device__ __forceinline__ int vt16_off(int d, int slot) {
 // (selection mode), the visit counters, then the selection list.
 template <int D>
 constexpr int lean_base_smem() {
-    return kLT * D * 2 + D * 32 + 2 * kLT * 4 + 2 * kLT * 4 + 16 * 3 * 8;
+    return kLT * D * 2 + D * 32 + 2 * kLT * 4 + 2 * kLT * 4 + 16 * 3 * 8 + 16 * 8;
 }
 
 // CP: cache policy of the decode K/V stream loads (0 default, 2 non-temporal).
@@ -63,7 +63,8 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     float* vsc_lds = ksc_lds + kLT;
     int* tcell = reinterpret_cast<int*>(vsc_lds + kLT);                       // [2][kLT]
     unsigned long long* dbg_lds = reinterpret_cast<unsigned long long*>(tcell + 2 * kLT);   // [16][3]
-    int* list = reinterpret_cast<int*>(dbg_lds + 16 * 3);
+    unsigned long long* tpath_lds = dbg_lds + 16 * 3;                                    // [16]
+    int* list = reinterpret_cast<int*>(tpath_lds + 16);
 
     const int lane = threadIdx.x;
     const int ln = lane & 15;
@@ -95,9 +96,15 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     else { r = row0; h = g * G + m; }
     if (!ok) { r = (MODE == kDecode) ? 0 : row0; h = g * G; }
     int pos, lim;
+    const bool tree = (MODE == kDecode) && p.tree != nullptr;
     if constexpr (MODE == kDecode) {
         pos = kvl - p.R + r;
-        lim = min(p.causal ? min(pos + 1, kvl) : kvl, hi);
+        lim = min((p.causal && !tree) ? min(pos + 1, kvl) : kvl, hi);
+        // tree windows: the window nodes this query vector sees, kept in LDS for the
+        // partial tiles (read after the first tile's barrier)
+        const unsigned long long path =
+            tree ? tree_path_mask_wave(p.tree + static_cast<int64_t>(b) * p.R, p.R, r) : ~0ull;
+        if (lg == 0) tpath_lds[ln] = path;
     } else {
         pos = p.q_pos ? p.q_pos[r] : 0;
         lim = 0x7fffffff;
@@ -195,9 +202,9 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         int lim_max = -1, lim_min = 0x7fffffff;
         const int m_end = min(p.M, m_wg + 16);
         for (int rr = m_wg / G; rr <= (m_end - 1) / G && rr < p.R; ++rr) {
-            const int l = p.causal ? min(kvl - p.R + rr + 1, kvl) : kvl;
+            const int l = (p.causal && !tree) ? min(kvl - p.R + rr + 1, kvl) : kvl;
             lim_max = max(lim_max, l);
-            lim_min = min(lim_min, l);
+            lim_min = min(lim_min, tree ? max(kvl - p.R, 0) : l);
         }
         n_keys = max(0, min(hi, lim_max) - lo);
         n_full = max(0, min(hi, lim_min) - lo);        // slots every query vector sees
@@ -412,6 +419,14 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         bool vis[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) vis[i] = full || (cell[i] >= 0 && cell[i] < lim);
+        if constexpr (MODE == kDecode) {
+            // window cells by path mask (all ones without a tree window)
+            const unsigned long long path = tpath_lds[ln];
+            const int ts = kvl - p.R;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vis[i] = vis[i] && (cell[i] < ts || ((path >> ((cell[i] - ts) & 63)) & 1ull));
+        }
         float sc[4] = {s[0], s[1], s[2], s[3]};
         if constexpr (B8) {
             const float4 k4 = *reinterpret_cast<const float4*>(ksc_lds + 4 * lg);
@@ -484,13 +499,17 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     tn |= wave_xor_i(tn, 32);
     const bool nan_run = tn != 0;
     if (!ok) return;
-    const bool bad = nan_run || m_true == kPosInf;
+    bool bad = nan_run || m_true == kPosInf;
+    const bool split = (MODE == kDecode) || p.n_splits > 1;
+    const float z = (!split && p.sinks) ? p.sinks[h] : kNegInf;    // sink logit, unsplit only
+    if (z != z || z == kPosInf) bad = true;
     const bool empty = !bad && m_true == kNegInf;
     // move o and l from the lazy reference to the true maximum
     float f = 1.f;
     if (!bad && !empty && m_use != m_true) f = exp2f((m_use - m_true) * kLog2e);
     l *= f;
-    const bool split = (MODE == kDecode) || p.n_splits > 1;
+    float fin = f / l;                          // unsplit: out = o * fin
+    if (!split && z != kNegInf && !bad && !empty) fin = sink_norm(m_use, m_true, l, z);
     int64_t pi;
     if constexpr (MODE == kDecode)
         pi = ((static_cast<int64_t>(b) * p.R + r) * p.Hq + h) * p.n_slices_max + t_split;
@@ -501,7 +520,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         const int d0 = db * 16 + 4 * lg;
         float4 o;
         if (!split) {
-            const float inv = f / l;
+            const float inv = fin;
             if (bad) o = float4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
             else if (empty) o = float4{0.f, 0.f, 0.f, 0.f};
             else o = float4{o_acc[db][0] * inv, o_acc[db][1] * inv, o_acc[db][2] * inv, o_acc[db][3] * inv};

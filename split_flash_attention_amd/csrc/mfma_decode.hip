@@ -23,6 +23,7 @@ hipError_t launch_mfma_decode(const sel_attn_decode_args& a, hipStream_t st) {
     p.R = a.n_row; p.cap = a.cap; p.kv_len = a.kv_len; p.causal = a.causal;
     p.slice_len = a.slice_len; p.n_slices_max = a.n_slices_max;
     p.part_o = a.part_o; p.part_ml = a.part_ml; p.dbg_visit = a.dbg_visit;
+    p.tree = a.tree_parent;
     const int n_sl = std::min(a.n_slices_max, (a.cap + a.slice_len - 1) / a.slice_len);
     p.n_units_x = n_sl;
     p.n_units_z = a.n_stream;

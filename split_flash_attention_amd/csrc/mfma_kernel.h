@@ -75,7 +75,48 @@ struct MParams {
     float* part_ml;
     int64_t* dbg_visit;
     int32_t* dbg_sel;
+    const int32_t* tree;       // decode: [S][R] parent tables of tree windows, or null
+    const float* sinks;        // prefill without splits: [Hq] sink logits, or null
 };
+
+// ---------------------------------------------------------------------------
+// Tree-shaped verify windows (TensorFold PR #2595, kernel contract: tree widths
+// with heap-order parents).  Node a of a window of R <= 64 nodes sees itself and
+// its ancestors; parent[a] must lie in [-1, a), anything else makes a a root.
+// Every lane of the wave calls this with uniform control flow.  Lane a < R builds
+// node a's path mask by pointer jumping: after k rounds its mask holds the first
+// 2^k nodes of the path and `up` the node 2^k steps above, so ceil(log2 R) rounds
+// cover every path.  Returns the path mask of node r (0 <= r < R).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned long long tree_path_mask_wave(const int32_t* parent, int R, int r) {
+    const int lane = threadIdx.x & 63;
+    int up = -1;
+    unsigned long long m = 0;
+    if (lane < R) {
+        const int x = parent[lane];
+        up = (x >= -1 && x < lane) ? x : -1;
+        m = 1ull << lane;
+    }
+    for (int span = 1; span < R; span <<= 1) {
+        const int src = up < 0 ? 0 : up;
+        const unsigned long long mu = wave_read64(m, src);
+        const int uu = __shfl(up, src, 64);
+        if (up >= 0) {
+            m |= mu;
+            up = uu;
+        }
+    }
+    return wave_read64(m, r);
+}
+
+// Final normalisation with a sink logit z (HartsyInference PR #910: one more
+// logit in the softmax, without a value).  The row's o is relative to reference
+// `ref`, its sum l relative to its true maximum m (finite); z is finite or -inf
+// (a NaN or +inf sink makes the row NaN before this is reached).  out = o * f.
+__device__ __forceinline__ float sink_norm(float ref, float m, float l, float z) {
+    const float big = z > m ? z : m;
+    return exp2f((ref - big) * kLog2e) / fmaf(l, exp2f((m - big) * kLog2e), exp2f((z - big) * kLog2e));
+}
 
 // ---------------------------------------------------------------------------
 // 16-bit conversions and LDS addressing
@@ -192,9 +233,13 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
     const int m_wg = qchunk * p.qpw;               // first query vector of the work-group
     const int m_wave = m_wg + wave * QB * 16;       // first of this wave
 
-    // query vector -> (row, head, position, causal limit)
+    // query vector -> (row, head, position, causal limit); tree windows: cells from
+    // tstart on are window nodes, visible by the query vector's path mask
     int qv_row[QB], qv_head[QB], qv_pos[QB], qv_lim[QB];
+    unsigned long long qv_path[QB];
     bool qv_ok[QB];
+    const bool tree = (MODE == kDecode) && p.tree != nullptr;
+    const int tstart = tree ? kvl - p.R : 0x7fffffff;
 #pragma unroll
     for (int k = 0; k < QB; ++k) {
         const int m = m_wave + 16 * k + ln;
@@ -210,9 +255,11 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
         qv_ok[k] = ok;
         qv_row[k] = r;
         qv_head[k] = h;
+        qv_path[k] = 0;
         if constexpr (MODE == kDecode) {
             qv_pos[k] = kvl - p.R + r;
-            qv_lim[k] = p.causal ? min(qv_pos[k] + 1, kvl) : kvl;
+            qv_lim[k] = (p.causal && !tree) ? min(qv_pos[k] + 1, kvl) : kvl;
+            if (tree) qv_path[k] = tree_path_mask_wave(p.tree + static_cast<int64_t>(b) * p.R, p.R, r);
         } else {
             qv_pos[k] = p.q_pos ? p.q_pos[r] : 0;
             qv_lim[k] = (MODE == kMask && p.causal) ? qv_pos[k] + 1 : 0x7fffffff;
@@ -306,7 +353,7 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
             const int r_last = rbase + (m_end - 1) / G;
             for (int r = r_first; r <= r_last && r < p.R; ++r) {
                 int l;
-                if constexpr (MODE == kDecode) l = p.causal ? min(kvl - p.R + r + 1, kvl) : kvl;
+                if constexpr (MODE == kDecode) l = (p.causal && !tree) ? min(kvl - p.R + r + 1, kvl) : kvl;
                 else l = p.causal ? (p.q_pos[r] + 1) : hi;
                 lim_max = max(lim_max, l);
             }
@@ -479,7 +526,8 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
             for (int e = 0; e < 8; ++e) {
                 const int kb = e >> 2, i = e & 3;
                 const int cell = cell_of[e];
-                bool v = cell >= 0 && cell < qv_lim[k];
+                bool v = cell >= 0 && cell < qv_lim[k] &&
+                         (cell < tstart || ((qv_path[k] >> (cell - tstart)) & 1ull));
                 float maskv = 0.f;
                 if constexpr (MODE == kMask) {
                     if (v) {
@@ -581,9 +629,10 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
         if (!qv_ok[k]) continue;
         const int r = qv_row[k], h = qv_head[k];
         const float m = m_run[k];
-        const bool bad = nan_run[k] || m == kPosInf;
-        const bool empty = !bad && m == kNegInf;
         const bool split = (MODE == kDecode) || p.n_splits > 1;
+        const float z = (!split && p.sinks) ? p.sinks[h] : kNegInf;    // sink logit, unsplit only
+        const bool bad = nan_run[k] || m == kPosInf || z != z || z == kPosInf;
+        const bool empty = !bad && m == kNegInf;
         int64_t pi;
         if constexpr (MODE == kDecode)
             pi = ((static_cast<int64_t>(b) * p.R + r) * p.Hq + h) * p.n_slices_max + t_split;
@@ -594,7 +643,7 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
             const int d0 = db * 16 + 4 * lg;
             float4 o;
             if (!split) {
-                const float inv = 1.f / l;
+                const float inv = (z != kNegInf && !bad && !empty) ? sink_norm(m, m, l, z) : 1.f / l;
                 if (bad) o = float4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
                 else if (empty) o = float4{0.f, 0.f, 0.f, 0.f};
                 else o = float4{o_acc[k][db][0] * inv, o_acc[k][db][1] * inv, o_acc[k][db][2] * inv,

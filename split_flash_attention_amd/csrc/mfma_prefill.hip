@@ -24,6 +24,7 @@ mk::MParams common(const sel_attn_prefill_args& a) {
     p.split_step = (a.n_kv + a.n_splits - 1) / a.n_splits;
     p.out = a.out; p.part_o = a.part_o; p.part_ml = a.part_ml;
     p.dbg_visit = a.dbg_visit; p.dbg_sel = a.dbg_sel;
+    p.sinks = a.sinks;
     return p;
 }
 

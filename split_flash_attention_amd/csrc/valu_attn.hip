@@ -58,6 +58,8 @@ struct ValuParams {
     float* part_ml;
     int64_t* dbg_visit;
     int32_t* dbg_sel;
+    const int32_t* tree;       // decode: [S][R] parent tables of tree windows, or null
+    const float* sinks;        // prefill without splits: [Hq] sink logits, or null
 };
 
 // LDS carve-up (bytes)
@@ -84,6 +86,7 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
     __shared__ float m_run[kQv], l_run[kQv], c_run[kQv];
     __shared__ int nan_run[kQv];
     __shared__ long long dbg[kQv][3];
+    __shared__ unsigned long long tpath[kQv];     // tree windows: window nodes each query vector sees
     __shared__ int scan[kThreads];
     __shared__ int n_ids_s;
 
@@ -144,6 +147,20 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
         c_run[tid] = 0.f;
         nan_run[tid] = 0;
         dbg[tid][0] = dbg[tid][1] = dbg[tid][2] = 0;
+        // Tree windows (TensorFold PR #2595, kernel contract: heap-order parents):
+        // the row's node and its ancestors; a parent entry outside [-1, a) ends the
+        // walk, and the node index falls at every step, so it ends within R steps.
+        unsigned long long path = 0;
+        if (p.mode == kDecode && p.tree && tid < nq) {
+            const int32_t* par = p.tree + static_cast<int64_t>(b) * p.R;
+            int a = qrow(tid);
+            while (a >= 0) {
+                path |= 1ull << a;
+                const int up = par[a];
+                a = (up >= -1 && up < a) ? up : -1;
+            }
+        }
+        tpath[tid] = path;
     }
 
     // ---- selection list: sort, drop invalid and repeated ids --------------
@@ -215,6 +232,10 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
     // visibility of cell c for query vector i (c >= 0)
     auto visible = [&](int i, int c) -> bool {
         if (p.mode == kDecode) {
+            if (p.tree) {
+                const int t0 = kvl - p.R;
+                return c < kvl && (c < t0 || ((tpath[i] >> (c - t0)) & 1ull));
+            }
             const int lim = p.causal ? min(qpos(i) + 1, kvl) : kvl;
             return c < lim;
         }
@@ -355,11 +376,20 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
             if (i >= nq) break;
             const int r = qrow(i), h = qhead(i);
             const float m = m_run[i], l = l_run[i];
-            const bool bad = nan_run[i] || m == kPosInf;
-            const bool empty = !bad && m == kNegInf;
             const bool split = p.mode == kDecode || p.n_splits > 1;
+            const float z = (!split && p.sinks) ? p.sinks[h] : kNegInf;   // sink logit, unsplit only
+            const bool bad = nan_run[i] || m == kPosInf || z != z || z == kPosInf;
+            const bool empty = !bad && m == kNegInf;
             if (!split) {
-                float o = bad ? __builtin_nanf("") : (empty ? 0.f : acc[u] / l);
+                // with a sink (HartsyInference PR #910): M = max(m, z), and the
+                // denominator gains exp(z - M)
+                float f = 1.f / l;
+                if (z != kNegInf && !bad && !empty) {
+                    const float big = max_keep(m, z);
+                    const float e = exp2f((m - big) * kLog2e);
+                    f = e / fmaf(l, e, exp2f((z - big) * kLog2e));
+                }
+                float o = bad ? __builtin_nanf("") : (empty ? 0.f : acc[u] * f);
                 p.out[(static_cast<int64_t>(r) * p.Hq + h) * D + d_own] = o;
             } else {
                 int64_t pi;
@@ -414,9 +444,12 @@ __global__ __launch_bounds__(256) void combine_kernel(sel_attn_combine_args a, i
     const float* po = a.part_o + unit * a.n_slices_max * D;
     float* out = a.out + unit * D;
 
-    // M = max over slices (NaN-aware)
-    bool nanf = false;
-    float M = kNegInf;
+    // M = max over slices and the sink logit (NaN-aware).  The sink (HartsyInference
+    // PR #910) is one more logit without a value: it enters M and the denominator.
+    const int h = static_cast<int>(unit % a.n_head_q);
+    const float z = a.sinks ? a.sinks[h] : kNegInf;
+    bool nanf = z != z;
+    float M = nanf ? kNegInf : z;
     for (int t = lane; t < ns; t += 64) {
         const float m = ml[2 * t];
         if (m != m) nanf = true;
@@ -471,6 +504,7 @@ __global__ __launch_bounds__(256) void combine_kernel(sel_attn_combine_args a, i
         num.w += __shfl_xor(num.w, msk, 64);
         den += __shfl_xor(den, msk, 64);
     }
+    if (z != kNegInf) den += exp2f((z - M) * kLog2e);
     if (sp == 0) reinterpret_cast<float4*>(out)[c] = float4{num.x / den, num.y / den, num.z / den, num.w / den};
 }
 
@@ -508,6 +542,7 @@ hipError_t launch_valu_decode(const sel_attn_decode_args& a, hipStream_t st) {
     p.slice_len = a.slice_len; p.n_slices_max = a.n_slices_max;
     p.n_qchunks = (a.n_row * p.G + kQv - 1) / kQv;
     p.part_o = a.part_o; p.part_ml = a.part_ml; p.dbg_visit = a.dbg_visit;
+    p.tree = a.tree_parent;
     const int n_sl = std::min(a.n_slices_max, (a.cap + a.slice_len - 1) / a.slice_len);
     dim3 grid(n_sl, a.n_head_kv * p.n_qchunks, a.n_stream);
     hipLaunchKernelGGL(valu_attn_kernel, grid, dim3(kThreads), kSmemBytes, st, p);
@@ -533,6 +568,7 @@ hipError_t launch_valu_prefill(const sel_attn_prefill_args& a, hipStream_t st) {
     p.rows_per_wg = a.sel ? 1 : std::max(1, kQv / p.G);
     p.out = a.out; p.part_o = a.part_o; p.part_ml = a.part_ml;
     p.dbg_visit = a.dbg_visit; p.dbg_sel = a.dbg_sel;
+    p.sinks = a.sinks;
     const int n_rb = (a.n_row + p.rows_per_wg - 1) / p.rows_per_wg;
     dim3 grid(a.n_splits, a.n_head_kv, n_rb);
     hipLaunchKernelGGL(valu_attn_kernel, grid, dim3(kThreads), kSmemBytes, st, p);

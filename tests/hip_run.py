@@ -49,6 +49,8 @@ class DecodeDev:
         self.vs = _t(wl.v_scale, device)
         self.kv_len = _t(wl.kv_len.astype(np.int32), device)
         self.alibi = _t(wl.alibi, device)
+        self.tree = _t(wl.tree_parent, device)
+        self.sinks = _t(wl.sinks, device)
         S, R, Hq, D = wl.q.shape
         self.ns = -(-wl.cap // self.slice_len)
         fill = float("nan") if poison_outputs else 0.0
@@ -67,11 +69,12 @@ class DecodeDev:
                               part_o=self.part_o, part_ml=self.part_ml, causal=wl.causal,
                               scale=wl.scale, softcap=wl.softcap, alibi=self.alibi,
                               slice_len=self.slice_len, k_scale=self.ks, v_scale=self.vs,
-                              dbg_visit=self.dbg if dbg else None)
+                              dbg_visit=self.dbg if dbg else None, tree_parent=self.tree)
 
     def combine_args(self):
         return sa.combine_args(part_o=self.part_o, part_ml=self.part_ml, out=self.out,
-                               kv_len=self.kv_len, slice_len=self.slice_len, cap=self.wl.cap)
+                               kv_len=self.kv_len, slice_len=self.slice_len, cap=self.wl.cap,
+                               sinks=self.sinks)
 
     def run(self, dbg=False, stream=None):
         self._keep = (self.args(dbg), self.combine_args())
@@ -101,6 +104,7 @@ class PrefillDev:
         self.alibi = _t(wl.alibi, device)
         self.sel = _t(wl.sel, device)
         self.mask = _t(wl.mask, device)
+        self.sinks = _t(wl.sinks, device)
         R, Hq, D = wl.q.shape
         fill = float("nan") if poison_outputs else 0.0
         self.out = torch.full((R, Hq, D), fill, dtype=torch.float32, device=device)
@@ -127,7 +131,7 @@ class PrefillDev:
                                k_scale=self.ks, v_scale=self.vs, n_splits=self.n_splits,
                                part_o=self.part_o, part_ml=self.part_ml,
                                dbg_visit=self.dbg if dbg else None,
-                               dbg_sel=self.dbg_sel if dbg else None)
+                               dbg_sel=self.dbg_sel if dbg else None, sinks=self.sinks)
 
     def run(self, dbg=False, stream=None):
         a = self.args(dbg)
@@ -135,7 +139,7 @@ class PrefillDev:
         sa.sel_attn_prefill(a, stream)
         if self.n_splits > 1:
             c = sa.combine_args(part_o=self.part_o, part_ml=self.part_ml,
-                                out=self.out.view(1, *self.out.shape))
+                                out=self.out.view(1, *self.out.shape), sinks=self.sinks)
             self._keep.append(c)
             sa.sel_attn_split_combine(c, stream)
 

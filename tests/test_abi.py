@@ -42,7 +42,7 @@ def test_struct_sizes_match(L):
     assert L.sel_attn_args_size(sa.OP_DECODE) == ctypes.sizeof(sa.DecodeArgs)
     assert L.sel_attn_args_size(sa.OP_PREFILL) == ctypes.sizeof(sa.PrefillArgs)
     assert L.sel_attn_args_size(sa.OP_COMBINE) == ctypes.sizeof(sa.CombineArgs)
-    assert L.sel_attn_abi_version() == 1
+    assert L.sel_attn_abi_version() == 2
     assert sa.strerror(sa.EWORKSPACE).startswith("partial buffer")
 
 
@@ -97,6 +97,10 @@ def test_good_arguments_are_supported(L):
                         kv_stride_cell=1024, kv_stride_head=256)
         assert sa.supports(sa.OP_DECODE, a)
         assert sa.decode_path(a) == 1                        # the matrix-core kernels take it
+    # tree windows up to 64 rows; sink logits on the combine and the unsplit prefill
+    assert sa.supports(sa.OP_DECODE, good_decode(tree_parent=FAKE, n_row=64))
+    assert sa.supports(sa.OP_COMBINE, good_combine(sinks=FAKE))
+    assert sa.supports(sa.OP_PREFILL, good_prefill(sinks=FAKE))
 
 
 @pytest.mark.parametrize("over,code", [
@@ -117,6 +121,7 @@ def test_good_arguments_are_supported(L):
     (dict(k=FAKE + 2), sa.EUNSUPPORTED),       # misaligned
     (dict(kv_stride_cell=1001), sa.EUNSUPPORTED),
     (dict(n_slices_max=31), sa.EWORKSPACE),    # 31 * 1024 < 32768
+    (dict(tree_parent=FAKE, n_row=65), sa.EUNSUPPORTED),   # one 64-bit path mask per row
 ])
 def test_decode_validation(L, over, code):
     a = good_decode(**over)

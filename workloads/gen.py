@@ -458,14 +458,16 @@ def config4(nan: bool = True) -> PrefillWorkload:
                              alibi=True, name="semantic_edge_prefill_f16" + ("" if nan else "_control"))
 
 
-def config5(depth: int = 32000) -> DecodeWorkload:
+def config5(depth: int = 32000, tree=None) -> DecodeWorkload:
     """INT8-cache verify decode: 16 streams x 16-row causal windows, 48/4 heads, D=256,
-    int8 rows + fp32 per-row scales, `depth` cached cells before the window, slices of 2048."""
+    int8 rows + fp32 per-row scales, `depth` cached cells before the window, slices of 2048.
+    tree="heap": each window is a binary tree in heap order instead of a chain."""
     variant = {12000: 0, 32000: 1}.get(depth, 2)
     w = 16
     return make_decode(seed=[5, variant], n_stream=16, n_row=w, n_head_q=48, n_head_kv=4,
                        head_dim=256, cap=depth + w, kv_dtype="i8", depths=[depth + w] * 16,
-                       causal=True, slice_len=2048, name=f"int8_verify_decode_d{depth}")
+                       causal=True, slice_len=2048, tree=tree,
+                       name=f"int8_{'tree_' if tree else ''}verify_decode_d{depth}")
 
 
 def sel_decode(n_head_q: int = 16, n_head_kv: int = 2, n_kv: int = 32048) -> PrefillWorkload:
@@ -487,5 +489,6 @@ CONFIGS = {
     "4c": lambda: config4(nan=False),
     "5a": lambda: config5(12000),
     "5b": lambda: config5(32000),
+    "5t": lambda: config5(32000, tree="heap"),
     "sd": sel_decode,
 }
