@@ -43,7 +43,7 @@ constexpr int lean_base_smem() {
 }
 
 // CP: cache policy of the decode K/V stream loads (0 default, 2 non-temporal).
-template <int MODE, int KT, int D, int CP>
+template <int MODE, int KT, int D, int CP, bool TREE>
 __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, const int gy, const int bz,
                                           char* smem) {
     constexpr bool F16 = (KT == SEL_ATTN_F16);
@@ -96,15 +96,16 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     else { r = row0; h = g * G + m; }
     if (!ok) { r = (MODE == kDecode) ? 0 : row0; h = g * G; }
     int pos, lim;
-    const bool tree = (MODE == kDecode) && p.tree != nullptr;
+    constexpr bool tree = (MODE == kDecode) && TREE;     // tree windows (launched when p.tree is set)
     if constexpr (MODE == kDecode) {
         pos = kvl - p.R + r;
         lim = min((p.causal && !tree) ? min(pos + 1, kvl) : kvl, hi);
         // tree windows: the window nodes this query vector sees, kept in LDS for the
-        // partial tiles (read after the first tile's barrier)
-        const unsigned long long path =
-            tree ? tree_path_mask_wave(p.tree + static_cast<int64_t>(b) * p.R, p.R, r) : ~0ull;
-        if (lg == 0) tpath_lds[ln] = path;
+        // tiles that reach the window (read after the first tile's barrier)
+        if constexpr (tree) {
+            const unsigned long long path = tree_path_mask_wave(p.tree + static_cast<int64_t>(b) * p.R, p.R, r);
+            if (lg == 0) tpath_lds[ln] = path;
+        }
     } else {
         pos = p.q_pos ? p.q_pos[r] : 0;
         lim = 0x7fffffff;
@@ -419,13 +420,14 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         bool vis[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) vis[i] = full || (cell[i] >= 0 && cell[i] < lim);
-        if constexpr (MODE == kDecode) {
-            // window cells by path mask (all ones without a tree window)
-            const unsigned long long path = tpath_lds[ln];
-            const int ts = kvl - p.R;
+        if constexpr (tree) {
+            if (!full) {                               // uniform: window cells by path mask
+                const unsigned long long path = tpath_lds[ln];
+                const int ts = kvl - p.R;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                vis[i] = vis[i] && (cell[i] < ts || ((path >> ((cell[i] - ts) & 63)) & 1ull));
+                for (int i = 0; i < 4; ++i)
+                    vis[i] = vis[i] && (cell[i] < ts || ((path >> ((cell[i] - ts) & 63)) & 1ull));
+            }
         }
         float sc[4] = {s[0], s[1], s[2], s[3]};
         if constexpr (B8) {
@@ -547,20 +549,20 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     }
 }
 
-template <int MODE, int KT, int D, int CP>
+template <int MODE, int KT, int D, int CP, bool TREE>
 __global__ __launch_bounds__(64, 2) void lean_attn_kernel(MParams p) {
     extern __shared__ __align__(16) char smem[];
     if constexpr (MODE == kDecode) {
         for_each_decode_item(p, [&](int t, int gy, int bz) {
-            lean_unit<MODE, KT, D, CP>(p, t, gy, bz, smem);
+            lean_unit<MODE, KT, D, CP, TREE>(p, t, gy, bz, smem);
             __syncthreads();
         });
     } else {
-        lean_unit<MODE, KT, D, CP>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+        lean_unit<MODE, KT, D, CP, TREE>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem);
     }
 }
 
-template <int MODE, int KT, int D, int CP>
+template <int MODE, int KT, int D, int CP, bool TREE>
 int lean_resident_groups(int smem) {
     static int cached[16] = {0};
     static int cached_smem[16] = {0};
@@ -570,7 +572,7 @@ int lean_resident_groups(int smem) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lean_attn_kernel<MODE, KT, D, CP>, 64, smem) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lean_attn_kernel<MODE, KT, D, CP, TREE>, 64, smem) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
@@ -580,39 +582,43 @@ int lean_resident_groups(int smem) {
     return cached[dev];
 }
 
-template <int MODE, int KT, int D, int CP>
+template <int MODE, int KT, int D, int CP, bool TREE>
 hipError_t lean_launch_one(const MParams& p, dim3 grid, hipStream_t st) {
     const int smem = lean_base_smem<D>() + (MODE == kSel ? p.sel_pow2 * 4 : 0);
     if constexpr (MODE == kDecode) {
         const long long items = static_cast<long long>(grid.x) * grid.y * grid.z;
-        grid = dim3(decode_grid(items, lean_resident_groups<MODE, KT, D, CP>(smem)), 1, 1);
+        grid = dim3(decode_grid(items, lean_resident_groups<MODE, KT, D, CP, TREE>(smem)), 1, 1);
     }
-    hipLaunchKernelGGL((lean_attn_kernel<MODE, KT, D, CP>), grid, dim3(64), smem, st, p);
+    hipLaunchKernelGGL((lean_attn_kernel<MODE, KT, D, CP, TREE>), grid, dim3(64), smem, st, p);
     return hipGetLastError();
 }
 
-template <int MODE, int KT, int CP>
+template <int MODE, int KT, int CP, bool TREE>
 hipError_t lean_launch_dim(const MParams& p, dim3 grid, hipStream_t st) {
-    return p.D == 256 ? lean_launch_one<MODE, KT, 256, CP>(p, grid, st)
-                      : lean_launch_one<MODE, KT, 128, CP>(p, grid, st);
+    return p.D == 256 ? lean_launch_one<MODE, KT, 256, CP, TREE>(p, grid, st)
+                      : lean_launch_one<MODE, KT, 128, CP, TREE>(p, grid, st);
 }
 
-template <int MODE, int CP>
+template <int MODE, int CP, bool TREE>
 hipError_t lean_launch_dt(int dt, const MParams& p, dim3 grid, hipStream_t st) {
-    if (dt == SEL_ATTN_BF16) return lean_launch_dim<MODE, SEL_ATTN_BF16, CP>(p, grid, st);
-    if (dt == SEL_ATTN_F16) return lean_launch_dim<MODE, SEL_ATTN_F16, CP>(p, grid, st);
-    if (dt == SEL_ATTN_I8) return lean_launch_dim<MODE, SEL_ATTN_I8, CP>(p, grid, st);
-    return lean_launch_dim<MODE, SEL_ATTN_FP8, CP>(p, grid, st);
+    if (dt == SEL_ATTN_BF16) return lean_launch_dim<MODE, SEL_ATTN_BF16, CP, TREE>(p, grid, st);
+    if (dt == SEL_ATTN_F16) return lean_launch_dim<MODE, SEL_ATTN_F16, CP, TREE>(p, grid, st);
+    if (dt == SEL_ATTN_I8) return lean_launch_dim<MODE, SEL_ATTN_I8, CP, TREE>(p, grid, st);
+    return lean_launch_dim<MODE, SEL_ATTN_FP8, CP, TREE>(p, grid, st);
 }
 
-// Decode streams each unit with non-temporal loads when one work-group reads it
-// (a single query chunk); selection mode and multi-chunk decode keep the default.
+// A decode unit is read by its one work-group (the kernel is launched with one
+// query chunk per kv head), so decode streams K/V with non-temporal loads;
+// selection mode keeps the default policy.  Tree windows get their own variant so
+// that the plain decode loop carries no path-mask work.
 template <int MODE>
 hipError_t lean_launch(int dt, const MParams& p, dim3 grid, hipStream_t st) {
     if constexpr (MODE == kDecode) {
-        if (p.n_units_y == p.Hkv) return lean_launch_dt<MODE, 2>(dt, p, grid, st);
+        if (p.tree) return lean_launch_dt<MODE, 2, true>(dt, p, grid, st);
+        return lean_launch_dt<MODE, 2, false>(dt, p, grid, st);
+    } else {
+        return lean_launch_dt<MODE, 0, false>(dt, p, grid, st);
     }
-    return lean_launch_dt<MODE, 0>(dt, p, grid, st);
 }
 
 }  // namespace mk
