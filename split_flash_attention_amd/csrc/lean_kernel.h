@@ -140,48 +140,85 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     int n_keys, n_full = 0;
     int id0 = 0;                               // selection: first list entry of this split
     if constexpr (MODE == kSel) {
-        // the row's list: invalid ids become +inf, bitonic sort in LDS, then the
-        // repeats are dropped by a wave-wide compaction (ballot + prefix count)
-        const int P = p.sel_pow2;
         const int32_t* srow = p.sel + static_cast<int64_t>(row0) * p.n_sel;
-        for (int e = lane; e < P; e += 64) {
-            int id = 0x7fffffff;
-            if (e < p.n_sel) {
+        int n_ids = 0;
+        // an id is valid iff 0 <= id < nblk
+        const int nblk = static_cast<int>((static_cast<int64_t>(p.n_kv) + p.bs - 1) / p.bs);
+        if (nblk <= kLT * D * 2 * 8) {
+            // the row's valid ids as a bitmap over the blocks (in the K tile's LDS,
+            // free until the first tile): set bits collapse repeats, and reading the
+            // words in order gives the ids sorted; a prefix count over the lanes
+            // places each word's ids
+            uint32_t* bm = reinterpret_cast<uint32_t*>(k_lds);
+            const int nw = (nblk + 31) >> 5;
+            for (int w = lane; w < nw; w += 64) bm[w] = 0u;
+            __syncthreads();
+            for (int e = lane; e < p.n_sel; e += 64) {
                 const int x = srow[e];
-                if (x >= 0 && static_cast<int64_t>(x) * p.bs < p.n_kv) id = x;
+                if (x >= 0 && x < nblk) atomicOr(&bm[x >> 5], 1u << (x & 31));
             }
-            list[e] = id;
-        }
-        __syncthreads();
-        for (int kq = 2; kq <= P; kq <<= 1) {
-            for (int j = kq >> 1; j > 0; j >>= 1) {
-                for (int e = lane; e < P; e += 64) {
-                    const int o = e ^ j;
-                    if (o > e) {
-                        const int x = list[e], y = list[o];
-                        if ((x > y) == ((e & kq) == 0)) { list[e] = y; list[o] = x; }
-                    }
+            __syncthreads();
+            for (int base = 0; base < nw; base += 64) {
+                const int w = base + lane;
+                uint32_t bits = w < nw ? bm[w] : 0u;
+                const int c = __popc(bits);
+                int incl = c;                               // inclusive prefix count over the wave
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const int t = __shfl_up(incl, d, 64);
+                    if (lane >= d) incl += t;
                 }
+                int pos = n_ids + incl - c;
+                while (bits) {
+                    list[pos++] = w * 32 + (__ffs(bits) - 1);
+                    bits &= bits - 1u;
+                }
+                n_ids += __shfl(incl, 63, 64);
+            }
+            __syncthreads();
+        } else {
+            // the row's list: invalid ids become +inf, bitonic sort in LDS, then the
+            // repeats are dropped by a wave-wide compaction (ballot + prefix count)
+            const int P = p.sel_pow2;
+            for (int e = lane; e < P; e += 64) {
+                int id = 0x7fffffff;
+                if (e < p.n_sel) {
+                    const int x = srow[e];
+                    if (x >= 0 && static_cast<int64_t>(x) * p.bs < p.n_kv) id = x;
+                }
+                list[e] = id;
+            }
+            __syncthreads();
+            for (int kq = 2; kq <= P; kq <<= 1) {
+                for (int j = kq >> 1; j > 0; j >>= 1) {
+                    for (int e = lane; e < P; e += 64) {
+                        const int o = e ^ j;
+                        if (o > e) {
+                            const int x = list[e], y = list[o];
+                            if ((x > y) == ((e & kq) == 0)) { list[e] = y; list[o] = x; }
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+            // keep element e if it is valid and differs from element e - 1; kept
+            // elements move down to their rank (never above their own index, and each
+            // block is read before it is written, so in place is safe)
+            int prev = -1;
+            for (int base = 0; base < P; base += 64) {
+                const int e = base + lane;
+                const int x = e < P ? list[e] : 0x7fffffff;
+                const int up = __shfl_up(x, 1, 64);          // every lane takes part in the exchange
+                const int before = lane > 0 ? up : prev;
+                const bool keep = x != 0x7fffffff && x != before;
+                const unsigned long long bal = __ballot(keep);
+                const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+                prev = __shfl(x, 63, 64);
+                __syncthreads();
+                if (keep) list[n_ids + rank] = x;
+                n_ids += __popcll(bal);
                 __syncthreads();
             }
-        }
-        // keep element e if it is valid and differs from element e - 1; kept
-        // elements move down to their rank (never above their own index, and each
-        // block is read before it is written, so in place is safe)
-        int n_ids = 0, prev = -1;
-        for (int base = 0; base < P; base += 64) {
-            const int e = base + lane;
-            const int x = e < P ? list[e] : 0x7fffffff;
-            const int up = __shfl_up(x, 1, 64);          // every lane takes part in the exchange
-            const int before = lane > 0 ? up : prev;
-            const bool keep = x != 0x7fffffff && x != before;
-            const unsigned long long bal = __ballot(keep);
-            const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-            prev = __shfl(x, 63, 64);
-            __syncthreads();
-            if (keep) list[n_ids + rank] = x;
-            n_ids += __popcll(bal);
-            __syncthreads();
         }
         if (p.dbg_sel && t_split == 0 && qchunk == 0) {
             int32_t* dst = p.dbg_sel + (static_cast<int64_t>(row0) * p.Hkv + g) * (1 + p.n_sel);

@@ -249,6 +249,32 @@ def test_prefill_selection_parity(dtype):
             assert dv[r, g, 0].tolist() == [c.size, int(c.sum()), int((c * c).sum())]
 
 
+@pytest.mark.parametrize("head_dim,n_kv,bs", [
+    (128, 32768, 1),     # 32768 blocks: the largest list the LDS block bitmap takes at D = 128
+    (128, 32769, 1),     # one block more: the sorting-network path
+    (256, 70001, 1),     # past the bitmap at D = 256 too
+    (256, 40000, 3),     # a partial last block
+])
+def test_prefill_selection_block_counts(head_dim, n_kv, bs):
+    """Both ways of ordering a row's ids (an LDS bitmap over the blocks when it fits,
+    else a sorting network) give the oracle's sorted unique ids and outputs."""
+    wl = sel_small(seed=[18, n_kv], dtype="bf16", n_row=8, head_dim=head_dim, n_kv=n_kv,
+                   n_sel=300, n_dup=15, n_invalid=6, block_size=bs, first_pos=n_kv - 8)
+    sel = wl.sel.copy()
+    last = (n_kv + bs - 1) // bs - 1
+    sel[0, :4] = [last, last, last + 1, 0]          # the last valid block, its repeat, the first invalid
+    wl.sel = sel
+    out, dev = hip_run.run_prefill(wl, dbg=True, return_dev=True)
+    nmse_check(out, oracle_prefill(wl), TOL["bf16"], f"sel blocks {n_kv}/{bs}")
+    _, ids = oracle.visited_prefill(n_kv=wl.n_kv, n_head_kv=wl.n_head_kv, sel=wl.sel,
+                                    block_size=wl.block_size)
+    dsel = dev.dbg_sel.cpu().numpy()
+    for r in range(wl.n_row):
+        for g in range(wl.n_head_kv):
+            n = int(dsel[r, g, 0])
+            assert n == ids[r].size and np.array_equal(dsel[r, g, 1:1 + n], ids[r]), (r, g)
+
+
 def test_prefill_selection_fp32_is_refused():
     # selection mode runs on the matrix-core kernel only; fp32 K/V is refused
     import split_flash_attention_amd as sa
