@@ -14,9 +14,13 @@ over 4-cell blocks) and reports its TFLOP/s (4*D flops per visited (row, head,
 key)), the selected-key decode (16 rows, one per sequence of a unified cache, with
 the same lists and block size, the key range split 32 ways, then the combine),
 and a plain device copy of 1 GiB (the achievable copy rate, and the
-calibration for the memory counters).  `--verify` adds the int8 verify-window
-decode (16 streams x 16 rows, 48/4 heads, depth 32000, slices of 2048) and the
-split-K decode with e4m3 K/V rows.
+calibration for the memory counters).  Beside them: per-launch median and
+minimum times, the selected-key prefill right after a 512 MiB write (cold
+Infinity Cache), measured roofs (a bf16 8192^3 matmul, and a gather probe that
+reads exactly the K/V blocks the selected-key prefill gathers), the tiny dense
+decode and the semantic-edge mask prefill.  `--verify` adds the int8
+verify-window decode (16 streams x 16 rows, 48/4 heads, depth 32000, slices of
+2048) with chain and tree windows, and the split-K decode with e4m3 K/V rows.
 
 Prints ONE JSON line.  Inputs are seeded synthetic data (no dataset).
 """
@@ -92,6 +96,78 @@ def timed(fn, steps, torch):
     e1.record(s)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def timed_each(fn, n, torch):
+    """Per-call ms of `fn` over n calls (HIP events around each call): (median, min)."""
+    import statistics
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(s)
+    for i in range(n):
+        fn()
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    d = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+    return statistics.median(d), min(d)
+
+
+def timed_cold(fn, flush, n, torch):
+    """Median ms of `fn` right after `flush` (a write larger than the Infinity Cache)."""
+    import statistics
+    s = torch.cuda.current_stream()
+    d = []
+    for _ in range(n):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        d.append(e0.elapsed_time(e1))
+    return statistics.median(d)
+
+
+def gather_roof(wl, k, v, torch, np):
+    """Achievable gather bandwidth for the selected-key workload's own access pattern:
+    the probe reads exactly the K and V blocks the kernel gathers (one kv head's 4 x 512 B
+    rows of each selected block), one (row, kv head) unit per wave in list order as the
+    kernel does, and nothing else."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "tests", "probe", "libgather_probe.so"))
+    lib.gather_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    n_blocks = -(-wl.n_kv // wl.block_size)
+    hkv = wl.n_head_kv
+    ents, starts = [], [0]
+    for r in range(wl.n_row):
+        ids = wl.sel[r].astype(np.int64)
+        ids = np.unique(ids[(ids >= 0) & (ids < n_blocks)])
+        for g in range(hkv):
+            kv_pair = np.stack([ids * hkv + g, (ids + n_blocks) * hkv + g], axis=1).reshape(-1)
+            ents.append(kv_pair)                            # K block, then V block (V follows K)
+            starts.append(starts[-1] + kv_pair.size)
+    idx = torch.from_numpy(np.concatenate(ents).astype(np.int32)).cuda()
+    ustart = torch.tensor(starts, dtype=torch.int32).cuda()
+    n_units = len(starts) - 1
+    kv = torch.cat([k.reshape(-1), v.reshape(-1)])          # [K cache][V cache], 16-bit elements
+    row_bytes = wl.head_dim * 2
+    groups = 1024
+    out = torch.empty(groups * 4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    best = 0.0
+    for unroll in (4, 8, 16):
+        def run():
+            rc = lib.gather_probe(kv.data_ptr(), idx.data_ptr(), ustart.data_ptr(), n_units, hkv,
+                                  wl.block_size * hkv * row_bytes, row_bytes, wl.block_size,
+                                  hkv * row_bytes, out.data_ptr(), groups, unroll, stream)
+            assert rc == 0, rc
+        run()
+        ms = timed_each(run, 10, torch)[1]
+        best = max(best, idx.numel() * wl.block_size * row_bytes / (ms * 1e-3) / 1e9)
+    return best
 
 
 def cpu_baseline_decode(wl, min_seconds=12.0):
@@ -190,6 +266,40 @@ def main():
     ms_prefill = timed(prefill, args.steps, torch)
     ms_copy = timed(copy, max(3, args.steps // 4), torch)
     ms_sd = timed(sel_decode, args.steps, torch)
+    dec_med, dec_min = timed_each(decode_only, args.steps, torch)
+    pre_med, pre_min = timed_each(prefill, args.steps, torch)
+    sd_med, sd_min = timed_each(sel_decode, args.steps, torch)
+
+    # ---- more figures: cold selected-key prefill, measured roofs, the small workloads --
+    log("cold runs, roofs and the small workloads")
+    flush_buf = torch.empty(1 << 27, dtype=torch.float32, device="cuda")       # 512 MiB
+    ms_prefill_cold = timed_cold(prefill, lambda: flush_buf.fill_(0.5), 5, torch)
+    del flush_buf
+    gather_gbs = gather_roof(wl3, d3.k, d3.v, torch, np)
+    mm_a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16).contiguous()
+    mm_b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16).contiguous()
+    mm_c = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    torch.matmul(mm_a, mm_b, out=mm_c)
+    ms_mm = timed_each(lambda: torch.matmul(mm_a, mm_b, out=mm_c), 10, torch)[1]
+    matmul_tflops = 2.0 * 8192 ** 3 / (ms_mm * 1e-3) / 1e12
+    del mm_a, mm_b, mm_c
+    wl1 = gen.config1()
+    d1 = hip_run.DecodeDev(wl1, "cuda", poison_outputs=False)
+    a1, c1 = d1.args(), d1.combine_args()
+
+    def step1():
+        sa.sel_attn_decode(a1)
+        sa.sel_attn_split_combine(c1)
+
+    step1()
+    c1_med, c1_min = timed_each(step1, args.steps, torch)
+    small4 = {}
+    for name, wl4 in (("4", gen.config4()), ("4c", gen.config4(nan=False))):
+        d4 = hip_run.PrefillDev(wl4, "cuda", poison_outputs=False)
+        a4 = d4.args()
+        sa.sel_attn_prefill(a4)
+        small4[name] = timed_each(lambda: sa.sel_attn_prefill(a4), args.steps, torch)
+        del d4
 
     cells = int(np.asarray(wl2.kv_len, np.int64).sum())
     kv_bytes = cells * wl2.n_head_kv * wl2.head_dim * 2 * 2          # K and V, bf16
@@ -239,18 +349,34 @@ def main():
                      "unit": "GB/s", "frac": round(gbs_kernel / HBM_PEAK_GBS, 4),
                      "traffic": decode_traffic(),
                      "kernel": "decode (lean_attn_kernel<0, 2, 256>: decode, bf16, D=256)",
-                     "kernel_ms": round(ms_decode, 5)},
+                     "kernel_ms": round(ms_decode, 5),
+                     "kernel_ms_median": round(dec_med, 5), "kernel_ms_min": round(dec_min, 5)},
         "sel_prefill": {"workload": "2048 rows x 512 block ids (4-cell blocks), 16/2 heads, D=256, bf16",
-                        "ms": round(ms_prefill, 5), "tflops": round(tflops3, 3),
+                        "ms": round(ms_prefill, 5), "ms_median": round(pre_med, 5),
+                        "ms_min": round(pre_min, 5), "ms_cold": round(ms_prefill_cold, 5),
+                        "tflops": round(tflops3, 3),
                         "mfma_peak_frac": round(tflops3 / BF16_PEAK_TFLOPS, 5),
                         "gathered_gbs": round(gather3 / (ms_prefill * 1e-3) / 1e9, 2),
+                        "gather_roof_gbs": round(gather_gbs, 1),
+                        "gather_roof_frac": round(gather3 / (ms_prefill * 1e-3) / 1e9 / gather_gbs, 4),
                         "tokens_per_s": round(wl3.n_row / (ms_prefill * 1e-3), 1),
                         "prefill_path": sa.prefill_path(a3)},
         "sel_decode": {"workload": f"16 rows x 512 block ids (4-cell blocks), 16/2 heads, D=256, bf16, "
                                    f"N=32048, {SEL_DECODE_SPLITS} key-range splits + combine",
-                       "ms": round(ms_sd, 5), "tflops": round(flops6 / (ms_sd * 1e-3) / 1e12, 3),
+                       "ms": round(ms_sd, 5), "ms_median": round(sd_med, 5), "ms_min": round(sd_min, 5),
+                       "tflops": round(flops6 / (ms_sd * 1e-3) / 1e12, 3),
                        "gathered_gbs": round(gather6 / (ms_sd * 1e-3) / 1e9, 2),
                        "tokens_per_s": round(wl6.n_row / (ms_sd * 1e-3), 1)},
+        "dense_decode_tiny": {"workload": "1 row, 4/1 heads, D=256, 64 fp32 keys, decode + combine",
+                              "us_median": round(c1_med * 1e3, 2), "us_min": round(c1_min * 1e3, 2)},
+        "semantic_edge_prefill": {"workload": "256 rows x 4096 keys, 16/4 heads, D=128, fp16, softcap, "
+                                              "ALiBi, F32 mask (with NaN K / control without)",
+                                  "us_median": round(small4["4"][0] * 1e3, 2),
+                                  "us_median_control": round(small4["4c"][0] * 1e3, 2)},
+        "roofs": {"hbm_peak_gbs": HBM_PEAK_GBS, "bf16_mfma_peak_tflops": BF16_PEAK_TFLOPS,
+                  "copy_gbs": round(2 * copy_src.numel() * 4 / (ms_copy * 1e-3) / 1e9, 1),
+                  "bf16_matmul_tflops": round(matmul_tflops, 1),
+                  "sel_gather_gbs": round(gather_gbs, 1)},
         "copy_gbs": round(2 * copy_src.numel() * 4 / (ms_copy * 1e-3) / 1e9, 1),
         "tokens_per_s": round(wl2.n_stream / (ms_step * 1e-3), 1),
     }
@@ -272,9 +398,14 @@ def main():
         flops5 = 0.0
         for r in range(wl5.n_row):
             flops5 += 4.0 * wl5.head_dim * wl5.n_head_q * wl5.n_stream * (int(wl5.kv_len[0]) - wl5.n_row + r + 1)
+        roof5 = max(bytes5 / (HBM_PEAK_GBS * 1e9), flops5 / (BF16_PEAK_TFLOPS * 1e12)) * 1e3   # ms
         result["verify_decode"] = {"workload": "int8 verify: 16 streams x 16 rows, 48/4 heads, D=256, depth 32000",
                                    "ms": round(ms5, 5), "gbs": round(bytes5 / (ms5 * 1e-3) / 1e9, 2),
-                                   "tflops": round(flops5 / (ms5 * 1e-3) / 1e12, 2)}
+                                   "hbm_peak_frac": round(bytes5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "tflops": round(flops5 / (ms5 * 1e-3) / 1e12, 2),
+                                   "mfma_peak_frac": round(flops5 / (ms5 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                   "binding_roof_frac": round(roof5 / ms5, 4),
+                                   "tokens_per_s": round(wl5.n_stream * wl5.n_row / (ms5 * 1e-3), 1)}
         del d5
         log("generating the int8 tree verify-window workload")
         wl5t = gen.config5(32000, tree="heap")

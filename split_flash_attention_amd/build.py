@@ -32,16 +32,23 @@ def _compile(src):
     return obj
 
 
-PROBE_SRC = os.path.join(os.path.dirname(HERE), "tests", "probe", "mfma_probe.hip")
-PROBE_OUT = os.path.join(os.path.dirname(HERE), "tests", "probe", "libmfma_probe.so")
+PROBE_DIR = os.path.join(os.path.dirname(HERE), "tests", "probe")
+PROBE_SRC = os.path.join(PROBE_DIR, "mfma_probe.hip")
+PROBE_OUT = os.path.join(PROBE_DIR, "libmfma_probe.so")
+GATHER_SRC = os.path.join(PROBE_DIR, "gather_probe.hip")
+GATHER_OUT = os.path.join(PROBE_DIR, "libgather_probe.so")
 
 
 def build_probe():
-    """The one-wave MFMA layout probe used by the GPU tests."""
-    cmd = [HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", PROBE_OUT]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("probe build failed:\n" + r.stderr)
+    """The one-wave MFMA layout probe used by the GPU tests, and the gather-bandwidth
+    probe the benchmark measures its selected-key roof with."""
+    for src, out in ((PROBE_SRC, PROBE_OUT), (GATHER_SRC, GATHER_OUT)):
+        if not os.path.exists(src):
+            continue
+        cmd = [HIPCC, *FLAGS, "-shared", src, "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"probe build failed for {src}:\n" + r.stderr)
     return PROBE_OUT
 
 

@@ -14,6 +14,7 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace selattn {
 namespace {
@@ -23,6 +24,7 @@ constexpr int kQv = 32;         // query vectors per work-group
 constexpr int kThreads = 256;
 constexpr int kMaxD = 256;
 constexpr int kMaxSel = 4096;
+constexpr int kStageU = 8;      // K/V elements per thread in flight while staging a tile
 
 enum Mode : int { kDecode = 0, kMask = 1, kSel = 2 };
 
@@ -277,37 +279,72 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
             __syncthreads();
             continue;
         }
-        // stage K and V of the keys somebody sees
-        for (int e = tid; e < kTile * D; e += kThreads) {
-            const int s = e / D, d = e % D;
-            const int c = cell_t[s];
-            float kx = 0.f, vx = 0.f;
-            if (c >= 0 && ((any >> s) & 1u)) {
-                const int64_t base = (p.mode == kDecode ? static_cast<int64_t>(b) * p.kv_ss : 0) +
-                                     static_cast<int64_t>(c) * p.kv_sc +
-                                     static_cast<int64_t>(g) * p.kv_sh;
-                kx = load_kv_elem(p.k, base + d, p.dt);
-                vx = load_kv_elem(p.v, base + d, p.dt);
-                if (p.dt == SEL_ATTN_I8 || p.dt == SEL_ATTN_FP8) {
-                    const int64_t sb = (p.mode == kDecode ? static_cast<int64_t>(b) * p.sc_ss : 0) +
-                                       static_cast<int64_t>(c) * p.sc_sc +
-                                       static_cast<int64_t>(g) * p.sc_sh;
-                    kx *= p.ksc[sb];
-                    vx *= p.vsc[sb];
+        // stage K and V of the keys somebody sees: kStageU elements per thread in
+        // flight (all loads of a batch issued before any store), storage type fixed
+        // per instantiation
+        auto stage = [&](auto dt_tag) {
+            constexpr int DT = decltype(dt_tag)::value;
+            for (int e0 = tid; e0 < kTile * D; e0 += kThreads * kStageU) {
+                float kx[kStageU], vx[kStageU];
+#pragma unroll
+                for (int u = 0; u < kStageU; ++u) {
+                    const int e = e0 + u * kThreads;
+                    kx[u] = 0.f;
+                    vx[u] = 0.f;
+                    if (e < kTile * D) {
+                        const int s = e / D, d = e % D;
+                        const int c = cell_t[s];
+                        if (c >= 0 && ((any >> s) & 1u)) {
+                            const int64_t base = (p.mode == kDecode ? static_cast<int64_t>(b) * p.kv_ss : 0) +
+                                                 static_cast<int64_t>(c) * p.kv_sc +
+                                                 static_cast<int64_t>(g) * p.kv_sh;
+                            kx[u] = load_kv_elem(p.k, base + d, DT);
+                            vx[u] = load_kv_elem(p.v, base + d, DT);
+                            if constexpr (DT == SEL_ATTN_I8 || DT == SEL_ATTN_FP8) {
+                                const int64_t sb = (p.mode == kDecode ? static_cast<int64_t>(b) * p.sc_ss : 0) +
+                                                   static_cast<int64_t>(c) * p.sc_sc +
+                                                   static_cast<int64_t>(g) * p.sc_sh;
+                                kx[u] *= p.ksc[sb];
+                                vx[u] *= p.vsc[sb];
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kStageU; ++u) {
+                    const int e = e0 + u * kThreads;
+                    if (e < kTile * D) {
+                        const int s = e / D, d = e % D;
+                        kt[s * (kMaxD + 1) + d] = kx[u];
+                        vt[s * kMaxD + d] = vx[u];
+                    }
                 }
             }
-            kt[s * (kMaxD + 1) + d] = kx;
-            vt[s * kMaxD + d] = vx;
+        };
+        switch (p.dt) {
+        case SEL_ATTN_F32: stage(std::integral_constant<int, SEL_ATTN_F32>{}); break;
+        case SEL_ATTN_F16: stage(std::integral_constant<int, SEL_ATTN_F16>{}); break;
+        case SEL_ATTN_BF16: stage(std::integral_constant<int, SEL_ATTN_BF16>{}); break;
+        case SEL_ATTN_FP8: stage(std::integral_constant<int, SEL_ATTN_FP8>{}); break;
+        default: stage(std::integral_constant<int, SEL_ATTN_I8>{}); break;
         }
         __syncthreads();
         // scores of visible pairs
         for (int e = tid; e < kQv * kTile; e += kThreads) {
             const int i = e / kTile, s = e % kTile;
             if (i >= nq || !((vis[i] >> s) & 1u)) continue;
-            float dot = 0.f;
+            // four partial sums (D is a multiple of 4), so the multiply-adds overlap
+            float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
             const float* qi = qs + i * kMaxD;
             const float* ks = kt + s * (kMaxD + 1);
-            for (int d = 0; d < D; ++d) dot = fmaf(qi[d], ks[d], dot);
+#pragma unroll 4
+            for (int d = 0; d < D; d += 4) {
+                d0 = fmaf(qi[d], ks[d], d0);
+                d1 = fmaf(qi[d + 1], ks[d + 1], d1);
+                d2 = fmaf(qi[d + 2], ks[d + 2], d2);
+                d3 = fmaf(qi[d + 3], ks[d + 3], d3);
+            }
+            const float dot = (d0 + d1) + (d2 + d3);
             const int c = cell_t[s];
             const float slope = p.alibi ? p.alibi[qhead(i)] : 0.f;
             const float mv = p.mode == kMask
@@ -359,11 +396,17 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
                 const int i = ig + u * NI;
                 if (i >= nq) break;
                 const uint32_t bits = vis[i];
-                float a = acc[u] * c_run[i];
-                for (int s = 0; s < kTile; ++s) {
-                    if ((bits >> s) & 1u) a = fmaf(ps[i * kTile + s], vt[s * kMaxD + d_own], a);
+                // four partial sums over the tile's keys; a key the query vector does
+                // not see is skipped (its V may hold anything)
+                float a0 = acc[u] * c_run[i], a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+                for (int s = 0; s < kTile; s += 4) {
+                    if ((bits >> s) & 1u) a0 = fmaf(ps[i * kTile + s], vt[s * kMaxD + d_own], a0);
+                    if ((bits >> (s + 1)) & 1u) a1 = fmaf(ps[i * kTile + s + 1], vt[(s + 1) * kMaxD + d_own], a1);
+                    if ((bits >> (s + 2)) & 1u) a2 = fmaf(ps[i * kTile + s + 2], vt[(s + 2) * kMaxD + d_own], a2);
+                    if ((bits >> (s + 3)) & 1u) a3 = fmaf(ps[i * kTile + s + 3], vt[(s + 3) * kMaxD + d_own], a3);
                 }
-                acc[u] = a;
+                acc[u] = (a0 + a1) + (a2 + a3);
             }
         }
         __syncthreads();
