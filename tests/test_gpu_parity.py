@@ -321,6 +321,42 @@ def test_prefill_selection_edge_lists():
     assert np.all(out[0] == 0)
 
 
+@pytest.mark.parametrize("case", ["max_list", "one_id", "big_blocks", "all_repeats", "unsorted_edges"])
+def test_prefill_selection_list_extremes(case):
+    """List shapes at the edges of the API: 4096 ids (the maximum), a single id,
+    64-cell blocks with a partial last block, one id repeated 4096 times, and a
+    list that names the first and last blocks among invalid ids of both kinds."""
+    if case == "max_list":
+        wl = sel_small(seed=22, n_row=6, n_kv=30000, n_sel=4096, n_dup=200, n_invalid=96,
+                       block_size=4, first_pos=29990)
+    elif case == "one_id":
+        wl = sel_small(seed=23, n_row=6, n_sel=1, n_dup=0, n_invalid=0)
+    elif case == "big_blocks":
+        wl = sel_small(seed=24, n_row=6, n_kv=3001, n_sel=30, n_dup=3, n_invalid=2, block_size=64,
+                       first_pos=2990)
+    elif case == "all_repeats":
+        wl = sel_small(seed=25, n_row=4, n_sel=8, n_dup=0, n_invalid=0)
+        wl.sel = np.repeat(np.array([[7], [0], [500], [250]], np.int32), 4096, axis=1)
+    else:
+        wl = sel_small(seed=26, n_row=4, n_sel=16, n_dup=0, n_invalid=0)
+        n_blocks = -(-wl.n_kv // wl.block_size)
+        sel = np.full((4, 16), -1, np.int32)
+        sel[:, 3] = n_blocks - 1
+        sel[:, 7] = 0
+        sel[:, 9] = n_blocks                       # one past the last valid block
+        sel[:, 11] = np.iinfo(np.int32).max        # far past the cache
+        sel[:, 12] = np.iinfo(np.int32).min
+        wl.sel = sel
+    out, dev = hip_run.run_prefill(wl, dbg=True, return_dev=True)
+    nmse_check(out, oracle_prefill(wl), TOL["bf16"], case)
+    _, ids = oracle.visited_prefill(n_kv=wl.n_kv, n_head_kv=wl.n_head_kv, sel=wl.sel,
+                                    block_size=wl.block_size)
+    dsel = dev.dbg_sel.cpu().numpy()
+    for r in range(wl.n_row):
+        n = int(dsel[r, 0, 0])
+        assert n == ids[r].size and np.array_equal(dsel[r, 0, 1:1 + n], ids[r]), (case, r)
+
+
 def test_prefill_selection_splits():
     wl = sel_small(seed=14, n_row=16)
     ref = oracle_prefill(wl)

@@ -85,6 +85,14 @@ TREE_CASES = {
     "bf16_random_w64": dict(n_stream=2, n_row=64, n_head_q=4, n_head_kv=1, head_dim=128,
                             cap=800, kv_dtype="bf16", depths=[800, 64], slice_len=256,
                             tree="random"),
+    # 64 rows x 8 heads = 512 query vectors: the work-group kernel in several query chunks
+    "bf16_random_w64_gqa8_chunks": dict(n_stream=2, n_row=64, n_head_q=16, n_head_kv=2, head_dim=128,
+                                        cap=700, kv_dtype="bf16", depths=[700, 70], slice_len=256,
+                                        tree="random"),
+    # caches shorter than the window: nodes before cell 0 do not exist
+    "i8_heap_w16_short_caches": dict(n_stream=3, n_row=16, n_head_q=48, n_head_kv=4, head_dim=256,
+                                     cap=40, kv_dtype="i8", depths=[40, 9, 1], slice_len=32,
+                                     tree="heap"),
     # fp32 K/V: the vector-ALU kernel
     "f32_random_w8_d64": dict(n_stream=2, n_row=8, n_head_q=8, n_head_kv=2, head_dim=64,
                               cap=100, kv_dtype="f32", depths=[100, 8], slice_len=32,
