@@ -490,11 +490,38 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
         for (int db = 0; db < NDB; ++db) o_acc[k][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    if (n_keys > 0) load_tile(0);
+    // Mask mode with one block of query vectors per wave: each lane's mask values of
+    // a tile (for the cells it scores, where its query vector may see them) are
+    // loaded a tile ahead, with the K/V rows.  With more blocks the registers are
+    // short, and the values are read where they are used.
+    constexpr bool MASK_AHEAD = MODE == kMask && QB == 1;
+    float mcur[MASK_AHEAD ? QB : 1][8], mnext[MASK_AHEAD ? QB : 1][8];
+    auto load_mask = [&](int t0, float (&mv)[MASK_AHEAD ? QB : 1][8]) {
+        if constexpr (MASK_AHEAD) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int cell = slot_cell(t0 + (e >> 2) * 16 + 4 * lg + (e & 3));
+#pragma unroll
+                for (int k = 0; k < QB; ++k)
+                    mv[k][e] = (cell >= 0 && cell < qv_lim[k])
+                                   ? p.mask[static_cast<int64_t>(qv_row[k]) * p.m_sr +
+                                            static_cast<int64_t>(qv_head[k]) * p.m_sh + cell]
+                                   : 0.f;
+            }
+        }
+    };
+
+    if (n_keys > 0) {
+        load_tile(0);
+        load_mask(0, mcur);
+    }
     for (int t0 = 0; t0 < n_keys; t0 += kTK) {
         store_tile();
         __syncthreads();
-        if (t0 + kTK < n_keys) load_tile(t0 + kTK);     // in flight during this tile's math
+        if (t0 + kTK < n_keys) {                          // in flight during this tile's math
+            load_tile(t0 + kTK);
+            load_mask(t0 + kTK, mnext);
+        }
 
         // ---- S^T = K . Q^T ----
         f32x4 s[QB][2];
@@ -531,8 +558,9 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                 float maskv = 0.f;
                 if constexpr (MODE == kMask) {
                     if (v) {
-                        maskv = p.mask[static_cast<int64_t>(qv_row[k]) * p.m_sr +
-                                       static_cast<int64_t>(qv_head[k]) * p.m_sh + cell];
+                        if constexpr (MASK_AHEAD) maskv = mcur[k][e];
+                        else maskv = p.mask[static_cast<int64_t>(qv_row[k]) * p.m_sr +
+                                            static_cast<int64_t>(qv_head[k]) * p.m_sh + cell];
                         v = maskv != kNegInf;
                     }
                 }
@@ -597,6 +625,12 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
             const u32x4 a = *reinterpret_cast<const u32x4*>(vt_lds + vt_off(db * 16 + ln, lg));
 #pragma unroll
             for (int k = 0; k < QB; ++k) o_acc[k][db] = mfma16x16x32<F16>(a, pop[k], o_acc[k][db]);
+        }
+        if constexpr (MASK_AHEAD) {
+#pragma unroll
+            for (int k = 0; k < QB; ++k)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) mcur[k][e] = mnext[k][e];
         }
         __syncthreads();
     }
