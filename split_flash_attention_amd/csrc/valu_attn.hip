@@ -354,40 +354,50 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
             ps[i * kTile + s] = score_pipeline(dot, p.scale, p.softcap, slope, c - qpos(i), mv);
         }
         __syncthreads();
-        // online softmax update, one thread per query vector
-        if (tid < nq) {
-            const int i = tid;
-            const uint32_t bits = vis[i];
-            float mt = kNegInf;
-            int nanf = nan_run[i];
-            for (int s = 0; s < kTile; ++s) {
-                if (!((bits >> s) & 1u)) continue;
-                const float x = ps[i * kTile + s];
-                if (x != x) nanf = 1;
-                else mt = max_keep(mt, x);
+        // online softmax update: a group of 32 threads per query vector, one thread
+        // per key of the tile, the maximum, NaN flag and sum reduced by lane exchanges
+        for (int i0 = 0; i0 < nq; i0 += kThreads / kTile) {
+            const int i = i0 + tid / kTile;
+            const int s = tid % kTile;
+            const bool live = i < nq;
+            const uint32_t bits = live ? vis[i] : 0u;
+            const bool v = (bits >> s) & 1u;
+            const float x = v ? ps[i * kTile + s] : kNegInf;
+            int nanf = (v && x != x) ? 1 : 0;
+            float mt = (v && x == x) ? x : kNegInf;
+#pragma unroll
+            for (int o = 1; o < kTile; o <<= 1) {
+                mt = max_keep(mt, __shfl_xor(mt, o, kTile));
+                nanf |= __shfl_xor(nanf, o, kTile);
             }
-            const float m_old = m_run[i];
+            const float m_old = live ? m_run[i] : kNegInf;
             const float m_new = max_keep(m_old, mt);
             const float c = rescale_factor(m_old, m_new);
-            float lsum = 0.f;
-            const bool first_head = ((p.mode == kDecode ? m0 + i : i) % G) == 0;
-            for (int s = 0; s < kTile; ++s) {
-                if (!((bits >> s) & 1u)) continue;
-                const float x = ps[i * kTile + s];
-                const float pe = exp_diff(x, m_new);
-                ps[i * kTile + s] = pe;
-                lsum += pe;
-                if (first_head) {
-                    const long long cc = cell_t[s];
-                    dbg[i][0] += 1;
-                    dbg[i][1] += cc;
-                    dbg[i][2] += cc * cc;
+            const float pe = v ? exp_diff(x, m_new) : 0.f;
+            if (v) ps[i * kTile + s] = pe;
+            float lsum = pe;
+#pragma unroll
+            for (int o = 1; o < kTile; o <<= 1) lsum += __shfl_xor(lsum, o, kTile);
+            if (live && s == 0) {
+                l_run[i] = l_run[i] * c + lsum;
+                m_run[i] = m_new;
+                c_run[i] = c;
+                nan_run[i] = nan_run[i] | nanf;
+                // visit counts of the row (its first query head), when asked for
+                if (p.dbg_visit && ((p.mode == kDecode ? m0 + i : i) % G) == 0) {
+                    long long n_vis = 0, sum_vis = 0, sq_vis = 0;
+                    for (int t = 0; t < kTile; ++t) {
+                        if (!((bits >> t) & 1u)) continue;
+                        const long long cc = cell_t[t];
+                        n_vis += 1;
+                        sum_vis += cc;
+                        sq_vis += cc * cc;
+                    }
+                    dbg[i][0] += n_vis;
+                    dbg[i][1] += sum_vis;
+                    dbg[i][2] += sq_vis;
                 }
             }
-            l_run[i] = l_run[i] * c + lsum;
-            m_run[i] = m_new;
-            c_run[i] = c;
-            nan_run[i] = nanf;
         }
         __syncthreads();
         // o = o * c + sum_s p_s v_s over visible keys only

@@ -431,6 +431,22 @@ def test_prefill_mask_dtypes_and_splits(dtype):
     nmse_check(hip_run.run_prefill(wl, n_splits=3), ref, TOL[dtype], f"mask {dtype} split")
 
 
+def test_valu_nan_propagation():
+    """fp32 K/V run on the vector-ALU kernel: NaN keys make exactly the query vectors
+    that see them NaN, in mask-mode prefill and in decode."""
+    wl = mask_small(nan=True, seed=19, kv_dtype="f32", n_row=24, n_kv=300, head_dim=64)
+    nmse_check(hip_run.run_prefill(wl), oracle_prefill(wl), TOL["f32"], "vector-ALU mask with NaN")
+    wl = gen.make_decode(seed=20, n_stream=2, n_row=3, n_head_q=8, n_head_kv=2, head_dim=64, cap=100,
+                         kv_dtype="f32", depths=[100, 60], slice_len=32)
+    k = wl.k.copy()
+    k[0, 40, 1, 3] = np.nan
+    k[1, 58, 0, 0] = np.nan                       # seen by rows 1 and 2 of stream 1 only
+    wl.k = k
+    out = hip_run.run_decode(wl)
+    nmse_check(out, oracle_decode(wl), TOL["f32"], "vector-ALU decode with NaN")
+    assert np.isfinite(out[1, 0]).all() and np.isnan(out[1, 1:, :4]).all()
+
+
 def test_finite_sentinel_and_bias_range_on_gpu():
     # the PR #910 controls at kernel level: a -1e30 row gives the uniform mean of V,
     # biases 100000/100001 give e/(1+e) weights (no F16 clamp)
