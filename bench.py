@@ -382,7 +382,26 @@ def main():
     }
 
     if args.verify:
-        log("generating the int8 verify-window workload")
+        log("generating the int8 verify-window workload at depth 12000")
+        wl5a = gen.config5(12000)
+        d5a = hip_run.DecodeDev(wl5a, "cuda", poison_outputs=False)
+        a5a, c5a = d5a.args(), d5a.combine_args()
+
+        def step5a():
+            sa.sel_attn_decode(a5a)
+            sa.sel_attn_split_combine(c5a)
+
+        step5a()
+        ms5a = timed(step5a, args.steps, torch)
+        bytes5a = int(np.asarray(wl5a.kv_len, np.int64).sum()) * wl5a.n_head_kv * (wl5a.head_dim + 4) * 2
+        flops5a = sum(4.0 * wl5a.head_dim * wl5a.n_head_q * wl5a.n_stream * (int(wl5a.kv_len[0]) - wl5a.n_row + r + 1)
+                      for r in range(wl5a.n_row))
+        result["verify_decode_d12000"] = {"workload": "int8 verify: 16 streams x 16 rows, 48/4 heads, D=256, depth 12000",
+                                          "ms": round(ms5a, 5), "gbs": round(bytes5a / (ms5a * 1e-3) / 1e9, 2),
+                                          "tflops": round(flops5a / (ms5a * 1e-3) / 1e12, 2),
+                                          "tokens_per_s": round(wl5a.n_stream * wl5a.n_row / (ms5a * 1e-3), 1)}
+        del d5a
+        log("generating the int8 verify-window workload at depth 32000")
         wl5 = gen.config5(32000)
         d5 = hip_run.DecodeDev(wl5, "cuda", poison_outputs=False)
         a5, c5 = d5.args(), d5.combine_args()

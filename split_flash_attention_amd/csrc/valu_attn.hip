@@ -25,6 +25,7 @@ constexpr int kThreads = 256;
 constexpr int kMaxD = 256;
 constexpr int kMaxSel = 4096;
 constexpr int kStageU = 8;      // K/V elements per thread in flight while staging a tile
+constexpr int kCombineRound = 8;   // partial slices per lane in flight in the combine
 
 enum Mode : int { kDecode = 0, kMask = 1, kSel = 2 };
 
@@ -522,14 +523,14 @@ __global__ __launch_bounds__(256) void combine_kernel(sel_attn_combine_args a, i
         }
         return;
     }
-    // eight slices per round: every load of the round is issued before any is used
+    // kCombineRound slices per round: every load of the round is issued before any is used
     float4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    for (int t0 = sp; t0 < ns; t0 += 8 * nph) {
-        float2 mlv[8];
-        float4 ov[8];
+    for (int t0 = sp; t0 < ns; t0 += kCombineRound * nph) {
+        float2 mlv[kCombineRound];
+        float4 ov[kCombineRound];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kCombineRound; ++j) {
             const int t = t0 + j * nph;
             if (t < ns) {
                 mlv[j] = reinterpret_cast<const float2*>(ml)[t];
@@ -540,7 +541,7 @@ __global__ __launch_bounds__(256) void combine_kernel(sel_attn_combine_args a, i
             }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kCombineRound; ++j) {
             if (mlv[j].x == kNegInf) continue;     // empty slice: contributes nothing
             const float w = exp2f((mlv[j].x - M) * kLog2e);
             den = fmaf(w, mlv[j].y, den);
