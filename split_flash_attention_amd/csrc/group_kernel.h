@@ -197,10 +197,10 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                     u32x4 w0, w1;
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        w0[2 * j] = bpair_bf16<KT>(rw[j], 0, rw[j], 1);
-                        w0[2 * j + 1] = bpair_bf16<KT>(rw[j], 2, rw[j], 3);
-                        w1[2 * j] = bpair_bf16<KT>(rw[2 + j], 0, rw[2 + j], 1);
-                        w1[2 * j + 1] = bpair_bf16<KT>(rw[2 + j], 2, rw[2 + j], 3);
+                        w0[2 * j] = kpair_bf16<KT>(rw[j], 0);
+                        w0[2 * j + 1] = kpair_bf16<KT>(rw[j], 1);
+                        w1[2 * j] = kpair_bf16<KT>(rw[2 + j], 0);
+                        w1[2 * j + 1] = kpair_bf16<KT>(rw[2 + j], 1);
                     }
                     *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch, D)) = w0;
                     *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch + 1, D)) = w1;
@@ -229,10 +229,12 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                     for (int h = 0; h < 2; ++h) {
                         const int wbc = (hc * 8 + 4 * h + c) * 64 + ((gq ^ ((2 * hc + h) & 3)) << 4) + 8 * kb;
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            const uint32_t lo2 = bpair_bf16<KT>(w[0][h], jj, w[1][h], jj);
-                            const uint32_t hi2 = bpair_bf16<KT>(w[2][h], jj, w[3][h], jj);
-                            *reinterpret_cast<uint2*>(vt_lds + (wbc ^ (jj << 6))) = uint2{lo2, hi2};
+                        for (int jj = 0; jj < 4; jj += 2) {          // bytes jj, jj + 1 at once
+                            uint32_t lo_e, lo_o, hi_e, hi_o;
+                            vpairs_bf16<KT>(w[0][h], w[1][h], jj >> 1, lo_e, lo_o);
+                            vpairs_bf16<KT>(w[2][h], w[3][h], jj >> 1, hi_e, hi_o);
+                            *reinterpret_cast<uint2*>(vt_lds + (wbc ^ (jj << 6))) = uint2{lo_e, hi_e};
+                            *reinterpret_cast<uint2*>(vt_lds + (wbc ^ ((jj + 1) << 6))) = uint2{lo_o, hi_o};
                         }
                     }
                 } else {

@@ -353,10 +353,10 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                     u32x4 w0, w1;
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        w0[2 * j] = bpair_bf16<KT>(rw[j], 0, rw[j], 1);
-                        w0[2 * j + 1] = bpair_bf16<KT>(rw[j], 2, rw[j], 3);
-                        w1[2 * j] = bpair_bf16<KT>(rw[2 + j], 0, rw[2 + j], 1);
-                        w1[2 * j + 1] = bpair_bf16<KT>(rw[2 + j], 2, rw[2 + j], 3);
+                        w0[2 * j] = kpair_bf16<KT>(rw[j], 0);
+                        w0[2 * j + 1] = kpair_bf16<KT>(rw[j], 1);
+                        w1[2 * j] = kpair_bf16<KT>(rw[2 + j], 0);
+                        w1[2 * j + 1] = kpair_bf16<KT>(rw[2 + j], 1);
                     }
                     *reinterpret_cast<u32x4*>(k_lds + k16_off(key, 2 * ch, D)) = w0;
                     *reinterpret_cast<u32x4*>(k_lds + k16_off(key, 2 * ch + 1, D)) = w1;
@@ -370,15 +370,22 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
             const int e = lane + 64 * i;
             if (e < V_TASKS) {
                 const int kg = e & 3, ch = e >> 2;
+                if constexpr (B8) {
+                    // dims dd, dd + 1 (bytes of half (dd >> 1) & 1 of word dd >> 2) at once
 #pragma unroll
-                for (int dd = 0; dd < EPC; ++dd) {
-                    uint32_t lo2, hi2;
-                    if constexpr (B8) {
-                        const int w = dd >> 2, by = dd & 3;
-                        lo2 = bpair_bf16<KT>(vreg[i][0][w], by, vreg[i][1][w], by);
-                        hi2 = bpair_bf16<KT>(vreg[i][2][w], by, vreg[i][3][w], by);
-                    } else {
+                    for (int dd = 0; dd < EPC; dd += 2) {
+                        const int w = dd >> 2, h = (dd >> 1) & 1;
+                        uint32_t lo_e, lo_o, hi_e, hi_o;
+                        vpairs_bf16<KT>(vreg[i][0][w], vreg[i][1][w], h, lo_e, lo_o);
+                        vpairs_bf16<KT>(vreg[i][2][w], vreg[i][3][w], h, hi_e, hi_o);
+                        *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd, kg)) = uint2{lo_e, hi_e};
+                        *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd + 1, kg)) = uint2{lo_o, hi_o};
+                    }
+                } else {
+#pragma unroll
+                    for (int dd = 0; dd < EPC; ++dd) {
                         const int w = dd >> 1;
+                        uint32_t lo2, hi2;
                         if (dd & 1) {
                             lo2 = (vreg[i][0][w] >> 16) | (vreg[i][1][w] & 0xffff0000u);
                             hi2 = (vreg[i][2][w] >> 16) | (vreg[i][3][w] & 0xffff0000u);
@@ -386,8 +393,8 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                             lo2 = (vreg[i][0][w] & 0xffffu) | (vreg[i][1][w] << 16);
                             hi2 = (vreg[i][2][w] & 0xffffu) | (vreg[i][3][w] << 16);
                         }
+                        *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd, kg)) = uint2{lo2, hi2};
                     }
-                    *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd, kg)) = uint2{lo2, hi2};
                 }
             }
         }

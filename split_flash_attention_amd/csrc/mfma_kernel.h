@@ -160,6 +160,35 @@ __device__ __forceinline__ uint32_t bpair_bf16(uint32_t wa, int ba, uint32_t wb,
                                  __float_as_uint(byte_float<KT>(wa, ba)), 0x07060302u);
 }
 
+// e4m3: the two bytes of half `hi` of word w as a packed bf16 pair, exact (every e4m3
+// value is a bf16 value): one v_cvt_scalef32_pk_bf16_fp8 with scale 1; the lower byte
+// lands in the low half
+__device__ __forceinline__ uint32_t fp8_pk_bf16(uint32_t w, bool hi) {
+    if (hi) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, true));
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, false));
+}
+
+// bf16 pair of bytes 2h and 2h + 1 of word w (one key, two adjacent dims)
+template <int KT>
+__device__ __forceinline__ uint32_t kpair_bf16(uint32_t w, int h) {
+    if constexpr (KT == SEL_ATTN_FP8) return fp8_pk_bf16(w, h != 0);
+    else return bpair_bf16<KT>(w, 2 * h, w, 2 * h + 1);
+}
+
+// bf16 pairs across keys a and b for the two dims of half h of their words:
+// even = {a, b} at dim 2h, odd = {a, b} at dim 2h + 1
+template <int KT>
+__device__ __forceinline__ void vpairs_bf16(uint32_t wa, uint32_t wb, int h, uint32_t& even, uint32_t& odd) {
+    if constexpr (KT == SEL_ATTN_FP8) {
+        const uint32_t pa = fp8_pk_bf16(wa, h != 0), pb = fp8_pk_bf16(wb, h != 0);
+        even = __builtin_amdgcn_perm(pb, pa, 0x05040100u);
+        odd = __builtin_amdgcn_perm(pb, pa, 0x07060302u);
+    } else {
+        even = bpair_bf16<KT>(wa, 2 * h, wb, 2 * h);
+        odd = bpair_bf16<KT>(wa, 2 * h + 1, wb, 2 * h + 1);
+    }
+}
+
 // byte offset of 16-byte chunk `ch` (8 dims) of key row `key` in the K tile; chunks
 // are XOR-ed with (key & 15) so the 16 rows of one operand read hit distinct banks
 __device__ __forceinline__ int k_off(int key, int ch, int D) {
@@ -428,10 +457,10 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                     u32x4 w0, w1;
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        w0[2 * j] = bpair_bf16<KT>(r[j], 0, r[j], 1);
-                        w0[2 * j + 1] = bpair_bf16<KT>(r[j], 2, r[j], 3);
-                        w1[2 * j] = bpair_bf16<KT>(r[2 + j], 0, r[2 + j], 1);
-                        w1[2 * j + 1] = bpair_bf16<KT>(r[2 + j], 2, r[2 + j], 3);
+                        w0[2 * j] = kpair_bf16<KT>(r[j], 0);
+                        w0[2 * j + 1] = kpair_bf16<KT>(r[j], 1);
+                        w1[2 * j] = kpair_bf16<KT>(r[2 + j], 0);
+                        w1[2 * j + 1] = kpair_bf16<KT>(r[2 + j], 1);
                     }
                     *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch, D)) = w0;
                     *reinterpret_cast<u32x4*>(k_lds + k_off(key, 2 * ch + 1, D)) = w1;

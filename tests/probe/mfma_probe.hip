@@ -43,6 +43,21 @@ __global__ void __launch_bounds__(64) fp8_cvt(const uint32_t* w, float* out) {
     out[l * 4 + 3] = __builtin_amdgcn_cvt_f32_fp8(x, 3);
 }
 
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1 (two adjacent e4m3 bytes -> two bf16),
+// both halves of each word; 256 lanes, out [256][2] packed pairs.
+__global__ void __launch_bounds__(256) fp8_pk_cvt(const uint32_t* w, uint32_t* out) {
+    const int l = threadIdx.x;
+    const int x = static_cast<int>(w[l]);
+    out[l * 2 + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+    out[l * 2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
+}
+
+extern "C" int fp8_pk_probe(const void* w, void* out, void* stream) {
+    hipLaunchKernelGGL(fp8_pk_cvt, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint32_t*>(w), static_cast<uint32_t*>(out));
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 extern "C" int fp8_probe(const void* w, void* out, void* stream) {
     hipLaunchKernelGGL(fp8_cvt, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
                        static_cast<const uint32_t*>(w), static_cast<float*>(out));

@@ -73,3 +73,29 @@ def test_fp8_convert_matches_e4m3_definition():
     assert np.array_equal(np.isnan(got), np.isnan(ref)), np.flatnonzero(np.isnan(got) != np.isnan(ref))
     fin = ~np.isnan(ref)
     assert np.array_equal(got[fin], ref[fin]), np.flatnonzero(got[fin] != ref[fin])
+
+
+def test_fp8_pair_convert_matches_e4m3_definition():
+    """v_cvt_scalef32_pk_bf16_fp8 with scale 1 (the pair widening the kernels use for
+    fp8 K/V): every code at every byte position gives the bf16 of its e4m3 value
+    exactly (e4m3 values are all representable in bf16), NaN for 0x7f and 0xff; the
+    low half of the result is the lower byte."""
+    if not torch.cuda.is_available():
+        pytest.fail("needs a GPU")
+    import oracle.attention as OA
+    lib = ctypes.CDLL(LIB)
+    lanes = np.arange(256)
+    codes = np.stack([(lanes + j) % 256 for j in range(4)], axis=1).astype(np.uint8)   # word l: l .. l + 3
+    w = torch.from_numpy(codes.reshape(-1).view(np.int32).copy()).cuda()
+    out = torch.zeros((256, 2), dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert lib.fp8_pk_probe(ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                            ctypes.c_void_p(st)) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32)
+    halves = np.stack([got[:, 0] & 0xFFFF, got[:, 0] >> 16, got[:, 1] & 0xFFFF, got[:, 1] >> 16], axis=1)
+    val = (halves.astype(np.uint32) << 16).view(np.float32).astype(np.float64)           # bf16 -> value
+    ref = OA.E4M3_TABLE[codes]
+    assert np.array_equal(np.isnan(val), np.isnan(ref)), np.argwhere(np.isnan(val) != np.isnan(ref))[:8]
+    fin = ~np.isnan(ref)
+    assert np.array_equal(val[fin], ref[fin]), np.argwhere((val != ref) & fin)[:8]
