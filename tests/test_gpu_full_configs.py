@@ -27,7 +27,9 @@ def _decode_streams(wl, idx):
                          kv_len=wl.kv_len[idx], causal=wl.causal, scale=wl.scale,
                          softcap=wl.softcap, alibi=wl.alibi,
                          k_scale=None if wl.k_scale is None else wl.k_scale[idx],
-                         v_scale=None if wl.v_scale is None else wl.v_scale[idx])
+                         v_scale=None if wl.v_scale is None else wl.v_scale[idx],
+                         tree_parent=None if wl.tree_parent is None else wl.tree_parent[idx],
+                         sinks=wl.sinks)
 
 
 def test_config2_split_k_decode_full():
@@ -48,6 +50,32 @@ def test_config5_int8_verify_full(depth):
     assert np.isfinite(out).all()
     idx = [0, 15]
     nmse_check(out[idx], _decode_streams(wl, idx), TOL["i8"], f"config5 depth {depth}")
+
+
+def test_config5_tree_verify_full():
+    """The int8 verify workload at depth 32000 with every window a 16-node binary tree in
+    heap order (the launch bench.py times), on two sampled streams, with the visited
+    cells of every row and slice of those streams."""
+    wl = gen.config5(32000, tree="heap")
+    out, dev = hip_run.run_decode(wl, dbg=True, return_dev=True)
+    assert np.isfinite(out).all()
+    idx = [0, 15]
+    nmse_check(out[idx], _decode_streams(wl, idx), TOL["i8"], "tree verify depth 32000")
+    st = oracle.visited_decode(kv_len=wl.kv_len[idx], n_row=wl.n_row, causal=True,
+                               slice_len=wl.slice_len, n_head_kv=wl.n_head_kv,
+                               tree_parent=wl.tree_parent[idx])
+    assert np.array_equal(dev.dbg.cpu().numpy()[idx], st)
+
+
+def test_config2_fp8_decode_full():
+    """The split-K workload with e4m3 rows and fp32 row scales (the launch bench.py
+    times), on the shallowest and deepest streams."""
+    wl = gen.config2(kv_dtype="fp8")
+    out = hip_run.run_decode(wl)
+    assert np.isfinite(out).all()
+    order = np.argsort(wl.kv_len)
+    idx = sorted({int(order[0]), int(order[-1])})
+    nmse_check(out[idx], _decode_streams(wl, idx), TOL["fp8"], "fp8 split-K sampled streams")
 
 
 def test_config3_selected_key_prefill_full():
