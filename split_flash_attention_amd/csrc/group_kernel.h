@@ -12,7 +12,8 @@
 //   * S^T = K . Q^T and O^T += V^T . P^T both on v_mfma_f32_16x16x32, each lane
 //     holding the 8 scores of one query vector that form its P^T operand;
 //   * the tile loads are spread over every thread of the work-group (K as 16-byte
-//     chunks, V as 4 keys x 8 bytes) and kept two tiles ahead in registers;
+//     chunks, V as 4 keys x 8 bytes) and kept two tiles ahead in registers with 4
+//     or 8 waves, one tile ahead with 12 (three waves share a SIMD's registers);
 //   * lazy rescaling of o and l as in lean_kernel.h: the exponent reference only
 //     moves when a score passes it by more than kLazy, the true maximum is applied
 //     once at the end (the correction exp(m_old - m_new) of TensorFold PR #985,
