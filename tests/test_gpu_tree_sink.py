@@ -73,9 +73,10 @@ TREE_CASES = {
     "fp8_heap_w1_gqa8": dict(n_stream=2, n_row=1, n_head_q=16, n_head_kv=2, head_dim=256,
                              cap=700, kv_dtype="fp8", depths=[700, 1], slice_len=256, tree="heap"),
     # more: the work-group kernel with 8 and 12 waves and two query chunks
-    "bf16_heap_w16_gqa8": dict(n_stream=3, n_row=16, n_head_q=16, n_head_kv=2, head_dim=256,
-                               cap=2100, kv_dtype="bf16", depths=[2100, 700, 17], slice_len=1024,
-                               tree="heap"),
+    "bf16_heap_w16_gqa8_softcap_alibi": dict(n_stream=3, n_row=16, n_head_q=16, n_head_kv=2,
+                                             head_dim=256, cap=2100, kv_dtype="bf16",
+                                             depths=[2100, 700, 17], slice_len=1024, tree="heap",
+                                             softcap=10.0, alibi=True),
     "i8_random_w12_gqa12": dict(n_stream=2, n_row=12, n_head_q=48, n_head_kv=4, head_dim=256,
                                 cap=1300, kv_dtype="i8", depths=[1300, 12], slice_len=512,
                                 tree="random"),
@@ -97,6 +98,10 @@ TREE_CASES = {
     "f32_random_w8_d64": dict(n_stream=2, n_row=8, n_head_q=8, n_head_kv=2, head_dim=64,
                               cap=100, kv_dtype="f32", depths=[100, 8], slice_len=32,
                               tree="random"),
+    # the tree replaces the causal flag: the same windows with causal off
+    "bf16_random_w8_noncausal_flag": dict(n_stream=2, n_row=8, n_head_q=16, n_head_kv=2,
+                                          head_dim=128, cap=600, kv_dtype="bf16", depths=[600, 50],
+                                          slice_len=256, tree="random", causal=False),
 }
 
 
