@@ -97,6 +97,16 @@ DECODE_CASES = {
                                         softcap=20.0, alibi=True),
     "bf16_verify_two_chunks": dict(n_stream=2, n_row=16, n_head_q=16, n_head_kv=1, head_dim=256,
                                    cap=600, kv_dtype="bf16", depths=[600, 100], slice_len=256),
+    # 12 waves (two K buffers in LDS): bf16 with softcap and ALiBi, f16 at D = 128
+    # with a ragged last block of query vectors, e4m3 at D = 256
+    "bf16_verify_w12_softcap_alibi": dict(n_stream=2, n_row=16, n_head_q=24, n_head_kv=2,
+                                          head_dim=256, cap=1100, kv_dtype="bf16",
+                                          depths=[1100, 47], slice_len=512, softcap=15.0,
+                                          alibi=True),
+    "f16_verify_w12_d128": dict(n_stream=2, n_row=11, n_head_q=16, n_head_kv=1, head_dim=128,
+                                cap=800, kv_dtype="f16", depths=[800, 95], slice_len=256),
+    "fp8_verify_w12_d256": dict(n_stream=1, n_row=12, n_head_q=16, n_head_kv=1, head_dim=256,
+                                cap=700, kv_dtype="fp8", depths=[700], slice_len=256),
     # e4m3 K/V rows with fp32 row scales: one block per unit, and a work-group unit
     "fp8_gqa8_d256": dict(n_stream=2, n_row=1, n_head_q=32, n_head_kv=4, head_dim=256,
                           cap=1800, kv_dtype="fp8", depths=[1800, 700], slice_len=512),
