@@ -399,9 +399,13 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         const u32x4 pop = u32x4{pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]),
                                 pack2<F16>(pv[4], pv[5]), pack2<F16>(pv[6], pv[7])};
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(vt_lds + vread[db & 1] + db * 1024);
-            o_acc[db] = mfma16x16x32<F16>(a, pop, o_acc[db]);
+        // two V^T operand reads in flight per pair of products (NDB is even): each
+        // product waits on its own read, so this halves the exposed LDS latency
+        for (int db = 0; db < NDB; db += 2) {
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(vt_lds + vread[0] + db * 1024);
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(vt_lds + vread[1] + (db + 1) * 1024);
+            o_acc[db] = mfma16x16x32<F16>(a0, pop, o_acc[db]);
+            o_acc[db + 1] = mfma16x16x32<F16>(a1, pop, o_acc[db + 1]);
         }
     };
 
