@@ -48,6 +48,7 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     constexpr int EPH = B8 ? 8 : 4;              // elements per 8-byte half chunk
     constexpr int ROWB = D * (B8 ? 1 : 2);
     static_assert(K_TASKS % 64 == 0 && V_TASKS % 64 == 0, "tasks must fill whole waves");
+    static_assert(NDB % 4 == 0, "O^T dim blocks are taken four at a time");
 
     char* k_lds = smem;                                            // kTK * D * 2
     char* vt_lds = smem + kTK * D * 2;                             // D * 64
@@ -399,13 +400,18 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         const u32x4 pop = u32x4{pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]),
                                 pack2<F16>(pv[4], pv[5]), pack2<F16>(pv[6], pv[7])};
 #pragma unroll
-        // two V^T operand reads in flight per pair of products (NDB is even): each
-        // product waits on its own read, so this halves the exposed LDS latency
-        for (int db = 0; db < NDB; db += 2) {
+        // four V^T operand reads per group of four products (NDB is a multiple of
+        // 4): each product waits on its own read, and with several in flight the
+        // LDS latency is paid once per group rather than once per product
+        for (int db = 0; db < NDB; db += 4) {
             const u32x4 a0 = *reinterpret_cast<const u32x4*>(vt_lds + vread[0] + db * 1024);
             const u32x4 a1 = *reinterpret_cast<const u32x4*>(vt_lds + vread[1] + (db + 1) * 1024);
+            const u32x4 a2 = *reinterpret_cast<const u32x4*>(vt_lds + vread[0] + (db + 2) * 1024);
+            const u32x4 a3 = *reinterpret_cast<const u32x4*>(vt_lds + vread[1] + (db + 3) * 1024);
             o_acc[db] = mfma16x16x32<F16>(a0, pop, o_acc[db]);
             o_acc[db + 1] = mfma16x16x32<F16>(a1, pop, o_acc[db + 1]);
+            o_acc[db + 2] = mfma16x16x32<F16>(a2, pop, o_acc[db + 2]);
+            o_acc[db + 3] = mfma16x16x32<F16>(a3, pop, o_acc[db + 3]);
         }
     };
 
