@@ -107,6 +107,11 @@ DECODE_CASES = {
                                 cap=800, kv_dtype="f16", depths=[800, 95], slice_len=256),
     "fp8_verify_w12_d256": dict(n_stream=1, n_row=12, n_head_q=16, n_head_kv=1, head_dim=256,
                                 cap=700, kv_dtype="fp8", depths=[700], slice_len=256),
+    "i8_verify_w12_d128": dict(n_stream=2, n_row=12, n_head_q=32, n_head_kv=2, head_dim=128,
+                               cap=650, kv_dtype="i8", depths=[650, 64], slice_len=256),
+    "fp8_verify_w12_d128_noncausal": dict(n_stream=1, n_row=16, n_head_q=12, n_head_kv=1,
+                                          head_dim=128, cap=520, kv_dtype="fp8", depths=[520],
+                                          slice_len=512, causal=False),
     # e4m3 K/V rows with fp32 row scales: one block per unit, and a work-group unit
     "fp8_gqa8_d256": dict(n_stream=2, n_row=1, n_head_q=32, n_head_kv=4, head_dim=256,
                           cap=1800, kv_dtype="fp8", depths=[1800, 700], slice_len=512),
