@@ -26,10 +26,13 @@ namespace selattn {
 namespace mk {
 
 // LDS: K tile, V^T tile, the tile's int8 scales, each wave's Q^T operands (16
-// query vectors x D, bf16/fp16, in operand order) and its visit counters.
-template <int D, int W>
+// query vectors x D, bf16/fp16, in operand order), its visit counters, its tree
+// path masks, its non-finite-V flag, and (16-bit and e4m3 data) the V^T indicator
+// tile of tiles seen in part.
+template <int D, int W, int KT>
 constexpr int group_smem() {
-    return kTK * D * 2 + D * 64 + 2 * kTK * 4 + W * D * 32 + W * 16 * 3 * 8 + W * 16 * 8;
+    return kTK * D * 2 + D * 64 + 2 * kTK * 4 + W * D * 32 + W * 16 * 3 * 8 + W * 16 * 8 + 16 * 4 +
+           (KT != SEL_ATTN_I8 ? D * 64 : 0);
 }
 
 template <int KT, int D, int W>
@@ -49,6 +52,10 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     constexpr int ROWB = D * (B8 ? 1 : 2);
     static_assert(K_TASKS % 64 == 0 && V_TASKS % 64 == 0, "tasks must fill whole waves");
     static_assert(NDB % 4 == 0, "O^T dim blocks are taken four at a time");
+    // Tiles that some query vectors see only in part (the window of a causal or tree
+    // verify) are staged with their non-finite V values split off (int8 data is
+    // always finite); see split_nonfinite.
+    constexpr bool CHK = KT != SEL_ATTN_I8;
 
     char* k_lds = smem;                                            // kTK * D * 2
     char* vt_lds = smem + kTK * D * 2;                             // D * 64
@@ -58,6 +65,8 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     unsigned long long* dbg_lds =                                  // W * 16 * 3
         reinterpret_cast<unsigned long long*>(q_lds + W * D * 32);
     unsigned long long* tpath_lds = dbg_lds + W * 16 * 3;          // W * 16
+    uint32_t* wflag = reinterpret_cast<uint32_t*>(tpath_lds + W * 16);   // [16]: wave w staged a non-finite V value
+    const int ind_off = static_cast<int>(reinterpret_cast<char*>(wflag + 16) - vt_lds);   // indicator tile - vt_lds
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -188,7 +197,9 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
             }
         }
     };
-    auto store_tile = [&](const Regs& rg) __attribute__((always_inline)) {
+    // chk: the tile is seen in part by some query vector, so its V is checked
+    auto store_tile = [&](const Regs& rg, bool chk) __attribute__((always_inline)) {
+        uint32_t nfa = 0u;
 #pragma unroll
         for (int i = 0; i < NSLOT; ++i) {
             const int e = tid + i * NT;
@@ -235,8 +246,13 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                             uint32_t lo_e, lo_o, hi_e, hi_o;
                             vpairs_bf16<KT>(w[0][h], w[1][h], jj >> 1, lo_e, lo_o);
                             vpairs_bf16<KT>(w[2][h], w[3][h], jj >> 1, hi_e, hi_o);
-                            *reinterpret_cast<uint2*>(vt_lds + (wbc ^ (jj << 6))) = uint2{lo_e, hi_e};
-                            *reinterpret_cast<uint2*>(vt_lds + (wbc ^ ((jj + 1) << 6))) = uint2{lo_o, hi_o};
+                            if (CHK && chk) {
+                                nfa = store_v_checked<F16>(vt_lds + (wbc ^ (jj << 6)), ind_off, lo_e, hi_e, nfa);
+                                nfa = store_v_checked<F16>(vt_lds + (wbc ^ ((jj + 1) << 6)), ind_off, lo_o, hi_o, nfa);
+                            } else {
+                                *reinterpret_cast<uint2*>(vt_lds + (wbc ^ (jj << 6))) = uint2{lo_e, hi_e};
+                                *reinterpret_cast<uint2*>(vt_lds + (wbc ^ ((jj + 1) << 6))) = uint2{lo_o, hi_o};
+                            }
                         }
                     }
                 } else {
@@ -253,7 +269,8 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                             hi2 = (w[2][wi] & 0xffffu) | (w[3][wi] << 16);
                         }
                     }
-                    *reinterpret_cast<uint2*>(vt_lds + vt_off(hc * EPH + dd, gq) + 8 * kb) = uint2{lo2, hi2};
+                    if (CHK && chk) nfa = store_v_checked<F16>(vt_lds + vt_off(hc * EPH + dd, gq) + 8 * kb, ind_off, lo2, hi2, nfa);
+                    else *reinterpret_cast<uint2*>(vt_lds + vt_off(hc * EPH + dd, gq) + 8 * kb) = uint2{lo2, hi2};
                 }
                 }
             }
@@ -264,7 +281,16 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                 vsc_lds[tid] = rg.vs;
             }
         }
+        if constexpr (CHK) {
+            if (chk) {                              // uniform
+                const bool any = wave_any(nfa != 0u);
+                if (lane == 0) wflag[wave] = any ? 1u : 0u;
+            }
+        }
     };
+    // tile t0 is seen in full by every query vector of the work-group
+    auto full_tile = [&](int t0) -> bool { return t0 + kTK <= n_full; };
+
 
     // ---- running state ---------------------------------------------------------
     float m_use = kNegInf;     // exponent reference of o and l
@@ -328,7 +354,7 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         // (uniform test) skips the per-score masks.  A NaN score is left out of the
         // maximum (v_max_f32 returns the other operand) and shows up as a NaN weight,
         // hence a NaN running sum, which the epilogue turns into the NaN flag.
-        const bool full = t0 + kTK <= n_full;
+        const bool full = full_tile(t0);
         // partial tile: bit o of vword says whether key slot o (cell cell0 + o) is visible
         uint32_t vword;
         {
@@ -394,8 +420,16 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         if constexpr (B8) {
             const float4 v0 = *reinterpret_cast<const float4*>(vsc_lds + 4 * lg);
             const float4 v1 = *reinterpret_cast<const float4*>(vsc_lds + 16 + 4 * lg);
-            pv[0] *= v0.x; pv[1] *= v0.y; pv[2] *= v0.z; pv[3] *= v0.w;
-            pv[4] *= v1.x; pv[5] *= v1.y; pv[6] *= v1.z; pv[7] *= v1.w;
+            const float vs[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            // the row scale joins visible weights only: a NaN scale of a key this query
+            // vector cannot see must not reach it
+            if (full) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] *= vs[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] = ((vword >> ((e >> 2) * 16 + (e & 3))) & 1u) ? pv[e] * vs[e] : 0.f;
+            }
         }
         const u32x4 pop = u32x4{pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]),
                                 pack2<F16>(pv[4], pv[5]), pack2<F16>(pv[6], pv[7])};
@@ -413,6 +447,31 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
             o_acc[db + 2] = mfma16x16x32<F16>(a2, pop, o_acc[db + 2]);
             o_acc[db + 3] = mfma16x16x32<F16>(a3, pop, o_acc[db + 3]);
         }
+        // a tile seen in part whose staged V held a non-finite value (uniform): the
+        // product above used its finite part; the visible non-finite values are
+        // counted from the indicator tile and applied
+        if constexpr (CHK) {
+            if (!full) {
+                uint32_t f = 0u;
+#pragma unroll
+                for (int w = 0; w < W; ++w) f |= wflag[w];
+                if (f != 0u) {
+                    bool vis[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vis[e] = (vword >> ((e >> 2) * 16 + (e & 3))) & 1u;
+                    const u32x4 pvis = u32x4{vis_pair<F16>(vis[0], vis[1]), vis_pair<F16>(vis[2], vis[3]),
+                                             vis_pair<F16>(vis[4], vis[5]), vis_pair<F16>(vis[6], vis[7])};
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const u32x4 ai = *reinterpret_cast<const u32x4*>(vt_lds + ind_off + vread[db & 1] + db * 1024);
+                        const f32x4 cnt = mfma16x16x32<F16>(ai, pvis, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o_acc[db][i] = apply_nonfinite(o_acc[db][i], cnt[i]);
+                        __builtin_amdgcn_sched_barrier(0);      // a rare path: one dim block at a time
+                    }
+                }
+            }
+        }
     };
 
     if constexpr (W < 12) {
@@ -421,13 +480,13 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         if (n_keys > 0) load_tile(ra, 0);
         if (n_keys > kTK) load_tile(rb, kTK);
         for (int t0 = 0; t0 < n_keys; t0 += 2 * kTK) {
-            store_tile(ra);
+            store_tile(ra, !full_tile(t0));
             __syncthreads();
             if (t0 + 2 * kTK < n_keys) load_tile(ra, t0 + 2 * kTK);
             if (wave_live) tile_math(t0);
             __syncthreads();
             if (t0 + kTK < n_keys) {
-                store_tile(rb);
+                store_tile(rb, !full_tile(t0 + kTK));
                 __syncthreads();
                 if (t0 + 3 * kTK < n_keys) load_tile(rb, t0 + 3 * kTK);
                 if (wave_live) tile_math(t0 + kTK);
@@ -440,7 +499,7 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         Regs ra;
         if (n_keys > 0) load_tile(ra, 0);
         for (int t0 = 0; t0 < n_keys; t0 += kTK) {
-            store_tile(ra);
+            store_tile(ra, !full_tile(t0));
             __syncthreads();
             if (t0 + kTK < n_keys) load_tile(ra, t0 + kTK);
             if (wave_live) tile_math(t0);
@@ -511,7 +570,7 @@ inline int group_waves(int nqb) {
 
 template <int KT, int D, int W>
 hipError_t group_launch_one(const MParams& p, dim3 grid, hipStream_t st) {
-    constexpr int smem = group_smem<D, W>();
+    constexpr int smem = group_smem<D, W, KT>();
     static int cached[16] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;

@@ -36,14 +36,20 @@ __device__ __forceinline__ int vt16_off(int d, int slot) {
 }
 
 // LDS: K tile, V^T tile, the tile's int8 scales, the cells of the next two tiles
-// (selection mode), the visit counters, then the selection list.
+// (selection mode), the visit counters, the tree path masks, then the selection
+// list (selection mode) or the V^T indicator tile (decode with mixed visibility).
 template <int D>
 constexpr int lean_base_smem() {
     return kLT * D * 2 + D * 32 + 2 * kLT * 4 + 2 * kLT * 4 + 16 * 3 * 8 + 16 * 8;
 }
+// The tiles of a unit may be seen in part by some of its query vectors (decode with
+// MIX), and their V may hold Inf or NaN (not int8).
+template <int MODE, int KT, bool MIX>
+constexpr bool lean_check(int) { return MODE == kDecode && MIX && KT != SEL_ATTN_I8; }
 
 // CP: cache policy of the decode K/V stream loads (0 default, 2 non-temporal).
-template <int MODE, int KT, int D, int CP, bool TREE>
+// MIX: decode rows of a unit may see different keys (several rows, causal or tree).
+template <int MODE, int KT, int D, int CP, bool TREE, bool MIX>
 __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, const int gy, const int bz,
                                           char* smem) {
     constexpr bool F16 = (KT == SEL_ATTN_F16);
@@ -56,6 +62,13 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     constexpr int NKL = (K_TASKS + 63) / 64;
     constexpr int NVL = (V_TASKS + 63) / 64;
     constexpr int EPC = B8 ? 16 : 8;
+    // MIX: the unit's rows see different keys (causal or tree windows of several
+    // rows).  Its tiles that some query vectors see only in part have their staged V
+    // staged with their non-finite V values split off into an indicator tile at
+    // vt_lds + IND (int8 data is always finite); see split_nonfinite.  In selection
+    // mode the query vectors of a wave are heads of one row.
+    constexpr bool CHK = lean_check<MODE, KT, MIX>(0);
+    constexpr int IND = lean_base_smem<D>() - kLT * D * 2;
 
     char* k_lds = smem;
     char* vt_lds = smem + kLT * D * 2;
@@ -342,7 +355,10 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
             }
         }
     };
-    auto store_tile = [&]() {
+    // chk: the tile is seen in part by some query vector, so its V is checked;
+    // returns (wave-uniform) whether a non-finite V value was staged
+    auto store_tile = [&](bool chk) -> bool {
+        uint32_t nfa = 0u;
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
             const int e = lane + 64 * i;
@@ -378,8 +394,13 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                         uint32_t lo_e, lo_o, hi_e, hi_o;
                         vpairs_bf16<KT>(vreg[i][0][w], vreg[i][1][w], h, lo_e, lo_o);
                         vpairs_bf16<KT>(vreg[i][2][w], vreg[i][3][w], h, hi_e, hi_o);
-                        *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd, kg)) = uint2{lo_e, hi_e};
-                        *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd + 1, kg)) = uint2{lo_o, hi_o};
+                        if (CHK && chk) {
+                            nfa = store_v_checked<F16>(vt_lds + vt16_off(ch * EPC + dd, kg), IND, lo_e, hi_e, nfa);
+                            nfa = store_v_checked<F16>(vt_lds + vt16_off(ch * EPC + dd + 1, kg), IND, lo_o, hi_o, nfa);
+                        } else {
+                            *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd, kg)) = uint2{lo_e, hi_e};
+                            *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd + 1, kg)) = uint2{lo_o, hi_o};
+                        }
                     }
                 } else {
 #pragma unroll
@@ -393,7 +414,8 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                             lo2 = (vreg[i][0][w] & 0xffffu) | (vreg[i][1][w] << 16);
                             hi2 = (vreg[i][2][w] & 0xffffu) | (vreg[i][3][w] << 16);
                         }
-                        *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd, kg)) = uint2{lo2, hi2};
+                        if (CHK && chk) nfa = store_v_checked<F16>(vt_lds + vt16_off(ch * EPC + dd, kg), IND, lo2, hi2, nfa);
+                        else *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd, kg)) = uint2{lo2, hi2};
                     }
                 }
             }
@@ -404,7 +426,10 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                 vsc_lds[lane] = vscr;
             }
         }
+        if constexpr (CHK) return chk && wave_any(nfa != 0u);
+        return false;
     };
+
 
     // ---- running state ---------------------------------------------------------
     float m_use = kNegInf;     // exponent reference of o and l
@@ -434,7 +459,9 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         load_tile(0);
     }
     for (int t0 = 0; t0 < n_keys; t0 += kLT) {
-        store_tile();
+        // uniform: every query vector sees the whole tile
+        const bool full = (MODE == kDecode) && t0 + kLT <= n_full;
+        const bool flagged = store_tile(!full);
         if (t0 + kLT < n_keys) fill_cells(t0 + kLT);
         __syncthreads();
         if (t0 + kLT < n_keys) load_tile(t0 + kLT);
@@ -451,15 +478,12 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         // (v_max_f32 returns the other operand) and shows up as a NaN weight, hence
         // a NaN running sum, which the epilogue turns into the NaN flag.
         int cell[4];
-        bool full;
         if constexpr (MODE == kSel) {
             const int4 c4 = *reinterpret_cast<const int4*>(tcell + ((t0 / kLT) & 1) * kLT + 4 * lg);
             cell[0] = c4.x; cell[1] = c4.y; cell[2] = c4.z; cell[3] = c4.w;
-            full = false;
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) cell[i] = lo + t0 + 4 * lg + i;
-            full = t0 + kLT <= n_full;                 // uniform: every query vector sees the tile
         }
         bool vis[4];
 #pragma unroll
@@ -524,14 +548,34 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
             l_run += pe[i];
         }
         if constexpr (B8) {
+            // the row scale joins visible weights only: a NaN scale of a key this query
+            // vector cannot see must not reach it
             const float4 v4 = *reinterpret_cast<const float4*>(vsc_lds + 4 * lg);
-            pe[0] *= v4.x; pe[1] *= v4.y; pe[2] *= v4.z; pe[3] *= v4.w;
+            const float vs[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pe[i] = vis[i] ? pe[i] * vs[i] : 0.f;
         }
         const u32x2 pop = u32x2{pack2<F16>(pe[0], pe[1]), pack2<F16>(pe[2], pe[3])};
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const u32x2 a = *reinterpret_cast<const u32x2*>(vt_lds + vread[db & 3] + db * 512);
             o_acc[db] = mfma16x16x16<F16>(a, pop, o_acc[db]);
+        }
+        if constexpr (CHK) {
+            // a tile seen in part whose staged V held a non-finite value: the product
+            // above used its finite part; the visible non-finite values are counted
+            // from the indicator tile and applied
+            if (flagged) {
+                const u32x2 pvis = u32x2{vis_pair<F16>(vis[0], vis[1]), vis_pair<F16>(vis[2], vis[3])};
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const u32x2 ai = *reinterpret_cast<const u32x2*>(vt_lds + IND + vread[db & 3] + db * 512);
+                    const f32x4 cnt = mfma16x16x16<F16>(ai, pvis, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o_acc[db][i] = apply_nonfinite(o_acc[db][i], cnt[i]);
+                    __builtin_amdgcn_sched_barrier(0);      // a rare path: one dim block at a time
+                }
+            }
         }
         __syncthreads();
     }
@@ -593,20 +637,20 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     }
 }
 
-template <int MODE, int KT, int D, int CP, bool TREE>
+template <int MODE, int KT, int D, int CP, bool TREE, bool MIX>
 __global__ __launch_bounds__(64, 2) void lean_attn_kernel(MParams p) {
     extern __shared__ __align__(16) char smem[];
     if constexpr (MODE == kDecode) {
         for_each_decode_item(p, [&](int t, int gy, int bz) {
-            lean_unit<MODE, KT, D, CP, TREE>(p, t, gy, bz, smem);
+            lean_unit<MODE, KT, D, CP, TREE, MIX>(p, t, gy, bz, smem);
             __syncthreads();
         });
     } else {
-        lean_unit<MODE, KT, D, CP, TREE>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+        lean_unit<MODE, KT, D, CP, TREE, MIX>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem);
     }
 }
 
-template <int MODE, int KT, int D, int CP, bool TREE>
+template <int MODE, int KT, int D, int CP, bool TREE, bool MIX>
 int lean_resident_groups(int smem) {
     static int cached[16] = {0};
     static int cached_smem[16] = {0};
@@ -616,7 +660,7 @@ int lean_resident_groups(int smem) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lean_attn_kernel<MODE, KT, D, CP, TREE>, 64, smem) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lean_attn_kernel<MODE, KT, D, CP, TREE, MIX>, 64, smem) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
@@ -626,42 +670,45 @@ int lean_resident_groups(int smem) {
     return cached[dev];
 }
 
-template <int MODE, int KT, int D, int CP, bool TREE>
+template <int MODE, int KT, int D, int CP, bool TREE, bool MIX>
 hipError_t lean_launch_one(const MParams& p, dim3 grid, hipStream_t st) {
-    const int smem = lean_base_smem<D>() + (MODE == kSel ? p.sel_pow2 * 4 : 0);
+    const int smem = lean_base_smem<D>() + (MODE == kSel ? p.sel_pow2 * 4 : 0) +
+                     (lean_check<MODE, KT, MIX>(0) ? D * 32 : 0);
     if constexpr (MODE == kDecode) {
         const long long items = static_cast<long long>(grid.x) * grid.y * grid.z;
-        grid = dim3(decode_grid(items, lean_resident_groups<MODE, KT, D, CP, TREE>(smem)), 1, 1);
+        grid = dim3(decode_grid(items, lean_resident_groups<MODE, KT, D, CP, TREE, MIX>(smem)), 1, 1);
     }
-    hipLaunchKernelGGL((lean_attn_kernel<MODE, KT, D, CP, TREE>), grid, dim3(64), smem, st, p);
+    hipLaunchKernelGGL((lean_attn_kernel<MODE, KT, D, CP, TREE, MIX>), grid, dim3(64), smem, st, p);
     return hipGetLastError();
 }
 
-template <int MODE, int KT, int CP, bool TREE>
+template <int MODE, int KT, int CP, bool TREE, bool MIX>
 hipError_t lean_launch_dim(const MParams& p, dim3 grid, hipStream_t st) {
-    return p.D == 256 ? lean_launch_one<MODE, KT, 256, CP, TREE>(p, grid, st)
-                      : lean_launch_one<MODE, KT, 128, CP, TREE>(p, grid, st);
+    return p.D == 256 ? lean_launch_one<MODE, KT, 256, CP, TREE, MIX>(p, grid, st)
+                      : lean_launch_one<MODE, KT, 128, CP, TREE, MIX>(p, grid, st);
 }
 
-template <int MODE, int CP, bool TREE>
+template <int MODE, int CP, bool TREE, bool MIX>
 hipError_t lean_launch_dt(int dt, const MParams& p, dim3 grid, hipStream_t st) {
-    if (dt == SEL_ATTN_BF16) return lean_launch_dim<MODE, SEL_ATTN_BF16, CP, TREE>(p, grid, st);
-    if (dt == SEL_ATTN_F16) return lean_launch_dim<MODE, SEL_ATTN_F16, CP, TREE>(p, grid, st);
-    if (dt == SEL_ATTN_I8) return lean_launch_dim<MODE, SEL_ATTN_I8, CP, TREE>(p, grid, st);
-    return lean_launch_dim<MODE, SEL_ATTN_FP8, CP, TREE>(p, grid, st);
+    if (dt == SEL_ATTN_BF16) return lean_launch_dim<MODE, SEL_ATTN_BF16, CP, TREE, MIX>(p, grid, st);
+    if (dt == SEL_ATTN_F16) return lean_launch_dim<MODE, SEL_ATTN_F16, CP, TREE, MIX>(p, grid, st);
+    if (dt == SEL_ATTN_I8) return lean_launch_dim<MODE, SEL_ATTN_I8, CP, TREE, MIX>(p, grid, st);
+    return lean_launch_dim<MODE, SEL_ATTN_FP8, CP, TREE, MIX>(p, grid, st);
 }
 
 // A decode unit is read by its one work-group (the kernel is launched with one
 // query chunk per kv head), so decode streams K/V with non-temporal loads;
-// selection mode keeps the default policy.  Tree windows get their own variant so
-// that the plain decode loop carries no path-mask work.
+// selection mode keeps the default policy.  Tree windows, and causal windows of
+// several rows (whose rows see different keys), get their own variants so that
+// the one-row decode loop carries neither path masks nor non-finite checks.
 template <int MODE>
 hipError_t lean_launch(int dt, const MParams& p, dim3 grid, hipStream_t st) {
     if constexpr (MODE == kDecode) {
-        if (p.tree) return lean_launch_dt<MODE, 2, true>(dt, p, grid, st);
-        return lean_launch_dt<MODE, 2, false>(dt, p, grid, st);
+        if (p.tree) return lean_launch_dt<MODE, 2, true, true>(dt, p, grid, st);
+        if (p.R > 1 && p.causal) return lean_launch_dt<MODE, 2, false, true>(dt, p, grid, st);
+        return lean_launch_dt<MODE, 2, false, false>(dt, p, grid, st);
     } else {
-        return lean_launch_dt<MODE, 0, false>(dt, p, grid, st);
+        return lean_launch_dt<MODE, 0, false, false>(dt, p, grid, st);
     }
 }
 

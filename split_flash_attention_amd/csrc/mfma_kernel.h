@@ -205,10 +205,88 @@ __device__ __forceinline__ int vt_off(int d, int cc) {
     return pr * 64 + ((cc ^ ((pr >> 2) & 3)) << 4);
 }
 
-template <int D, bool SEL>
-constexpr int smem_bytes() {
-    return kTK * D * 2 + D * 64 + 2 * kTK * 4 + (SEL ? kMaxSelM * 4 : 0);
+// ---------------------------------------------------------------------------
+// Keys some query vectors of a tile see and others do not.  O^T += V^T . P^T gives
+// such a key a zero weight for the query vectors that exclude it, and 0 * NaN or
+// 0 * Inf is NaN: a non-finite V value would leak into outputs that must never
+// read it (strix-llama.cpp PR #115, "Measurements": with poison=1 the masked cells
+// are skipped, not weighted with zero).  In a tile whose visibility differs
+// between the query vectors, staging therefore writes V^T with every Inf / NaN
+// half replaced by +0 (the product over it is the finite part, exact) and, beside
+// it, an indicator tile of the same layout: 1 for NaN, 64 for +Inf, 4096 for -Inf.
+// When a tile held a non-finite value, the indicator tile times the visibility of
+// each key (1 or 0) counts, per output, the visible NaN, +Inf and -Inf values, and
+// those counts turn the output into NaN or +-Inf as the sum over the visible keys
+// would.  Tiles every query vector sees in full, and int8 data (always finite),
+// are staged as they are.
+// ---------------------------------------------------------------------------
+
+// Splits a word of two packed 16-bit V values into its finite part (Inf and NaN
+// halves replaced by +0) and the indicator of its non-finite halves (1 for NaN, 64
+// for +Inf, 4096 for -Inf, as exact 16-bit floats; 0 for finite halves).  A product
+// of indicators with 0/1 weights over at most 32 keys is an exact integer below
+// 2^24 whose base-64 digits count the three kinds.
+template <bool F16>
+__device__ __forceinline__ void split_nonfinite(uint32_t w, uint32_t& fin, uint32_t& ind) {
+    constexpr uint32_t EXP = F16 ? 0x7C00u : 0x7F80u;
+    constexpr uint32_t MAN = F16 ? 0x03FFu : 0x007Fu;
+    constexpr uint32_t ONE = F16 ? 0x3C00u : 0x3F80u;     // 1
+    constexpr uint32_t C64 = F16 ? 0x5400u : 0x4280u;     // 64
+    constexpr uint32_t C4K = F16 ? 0x6C00u : 0x4580u;     // 4096
+    fin = 0u;
+    ind = 0u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t x = (w >> (16 * h)) & 0xffffu;
+        const bool nf = (x & EXP) == EXP;
+        const uint32_t c = (x & MAN) ? ONE : ((x & 0x8000u) ? C4K : C64);
+        fin |= (nf ? 0u : x) << (16 * h);
+        ind |= (nf ? c : 0u) << (16 * h);
+    }
 }
+
+// Packed 16-bit 1 / 0 pair: the visibility weights of the indicator product.
+template <bool F16>
+__device__ __forceinline__ uint32_t vis_pair(bool a, bool b) {
+    constexpr uint32_t ONE = F16 ? 0x3C00u : 0x3F80u;
+    return (a ? ONE : 0u) | ((b ? ONE : 0u) << 16);
+}
+
+// Output element o after a tile whose visible non-finite V values were counted as
+// cnt (base-64 digits: NaN, +Inf, -Inf): adds NaN, +Inf and/or -Inf as the plain
+// sum over the visible keys would (a +Inf and a -Inf together give NaN).
+__device__ __forceinline__ float apply_nonfinite(float o, float cnt) {
+    const int v = static_cast<int>(cnt);
+    if (v == 0) return o;
+    float add = 0.f;
+    if (v & 63) add = __builtin_nanf("");
+    else {
+        if ((v >> 6) & 63) add += kPosInf;
+        if (v >> 12) add += kNegInf;
+    }
+    return o + add;
+}
+
+// Stores one V^T word of a tile that is seen in part: the finite part at `at`, the
+// indicator at `at + ind_off`; returns `nfa` with the indicator OR-ed in.
+template <bool F16>
+__device__ __forceinline__ uint32_t store_v_checked(char* at, int ind_off, uint32_t lo, uint32_t hi, uint32_t nfa) {
+    uint32_t flo, ilo, fhi, ihi;
+    split_nonfinite<F16>(lo, flo, ilo);
+    split_nonfinite<F16>(hi, fhi, ihi);
+    *reinterpret_cast<uint2*>(at) = uint2{flo, fhi};
+    *reinterpret_cast<uint2*>(at + ind_off) = uint2{ilo, ihi};
+    return nfa | ilo | ihi;
+}
+
+// LDS: K tile, V^T tile, the tile's row scales, the waves' non-finite flags, then
+// the selection list (selection mode) or the V^T indicator tile (CHK kernels).
+template <int D, bool SEL, bool CHK>
+constexpr int smem_bytes() {
+    return kTK * D * 2 + D * 64 + 2 * kTK * 4 + 16 * 4 + (SEL ? kMaxSelM * 4 : 0) + (CHK ? D * 64 : 0);
+}
+template <int MODE, int KT>
+constexpr bool check_v(int) { return MODE != kSel && KT != SEL_ATTN_I8; }
 
 // ---------------------------------------------------------------------------
 // the kernel
@@ -230,12 +308,19 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
     constexpr int NKL = (K_TASKS + NT - 1) / NT;
     constexpr int NVL = (V_TASKS + NT - 1) / NT;
     constexpr int EPC = B8 ? 16 : 8;             // elements per 16-byte chunk
+    // Visibility may differ between the query vectors of a tile in decode and mask
+    // mode (causal or tree windows, per-row masks): their staged V is checked for
+    // non-finite values (int8 data is always finite).  In selection mode every query
+    // vector of a work-group belongs to one row and sees the same keys.
+    constexpr bool CHK = check_v<MODE, KT>(0);
 
     char* k_lds = smem;                                            // kTK * D * 2
     char* vt_lds = smem + kTK * D * 2;                             // D * 64
     float* ksc_lds = reinterpret_cast<float*>(vt_lds + D * 64);    // kTK
     float* vsc_lds = ksc_lds + kTK;                                // kTK
-    int* list = reinterpret_cast<int*>(vsc_lds + kTK);             // kMaxSelM (selection)
+    uint32_t* wflag = reinterpret_cast<uint32_t*>(vsc_lds + kTK);  // [16]: wave w staged a non-finite V value
+    int* list = reinterpret_cast<int*>(wflag + 16);                // kMaxSelM (selection)
+    constexpr int IND = kTK * D * 2 + D * 64 + 2 * kTK * 4 + 16 * 4 - kTK * D * 2;   // indicator tile - vt_lds
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -445,8 +530,10 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
             }
         }
     };
-    // registers -> LDS (K swizzled row-major, V transposed in contraction order)
+    // registers -> LDS (K swizzled row-major, V transposed in contraction order);
+    // with CHK, each wave records whether it staged a non-finite V value
     auto store_tile = [&]() {
+        uint32_t nfa = 0u;
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
             const int e = tid + i * NT;
@@ -492,7 +579,8 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                             hi2 = (vreg[i][2][w] & 0xffffu) | (vreg[i][3][w] << 16);
                         }
                     }
-                    *reinterpret_cast<uint2*>(vt_lds + vt_off(ch * EPC + dd, gq) + 8 * kb) = uint2{lo2, hi2};
+                    if constexpr (CHK) nfa = store_v_checked<F16>(vt_lds + vt_off(ch * EPC + dd, gq) + 8 * kb, IND, lo2, hi2, nfa);
+                    else *reinterpret_cast<uint2*>(vt_lds + vt_off(ch * EPC + dd, gq) + 8 * kb) = uint2{lo2, hi2};
                 }
             }
         }
@@ -502,7 +590,12 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                 vsc_lds[tid] = vscr;
             }
         }
+        if constexpr (CHK) {
+            const bool any = wave_any(nfa != 0u);
+            if (lane == 0) wflag[wave] = any ? 1u : 0u;
+        }
     };
+
 
     // ---- running state ---------------------------------------------------------
     float m_run[QB], l_run[QB];
@@ -547,6 +640,14 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
     for (int t0 = 0; t0 < n_keys; t0 += kTK) {
         store_tile();
         __syncthreads();
+        // a non-finite V value in this tile: P.V on the vector ALU with exact skips
+        bool flagged = false;
+        if constexpr (CHK) {
+            uint32_t f = 0u;
+#pragma unroll
+            for (int w = 0; w < W; ++w) f |= wflag[w];
+            flagged = f != 0u;
+        }
         if (t0 + kTK < n_keys) {                          // in flight during this tile's math
             load_tile(t0 + kTK);
             load_mask(t0 + kTK, mnext);
@@ -572,8 +673,10 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
         for (int e = 0; e < 8; ++e) cell_of[e] = slot_cell(t0 + (e >> 2) * 16 + 4 * lg + (e & 3));
 
         u32x4 pop[QB];
+        u32x4 pvis[QB];                 // flagged tiles: 0/1 visibility weights per block
 #pragma unroll
         for (int k = 0; k < QB; ++k) {
+            pvis[k] = u32x4{0u, 0u, 0u, 0u};
             float sc[8];
             bool vis[8];
             float tmax = kNegInf;
@@ -631,11 +734,18 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float w = pe[e];
-                if constexpr (B8) w *= vsc_lds[(e >> 2) * 16 + 4 * lg + (e & 3)];
+                // the row scale joins visible weights only (a NaN scale of a key this
+                // query vector cannot see must not reach it)
+                if constexpr (B8) w = vis[e] ? w * vsc_lds[(e >> 2) * 16 + 4 * lg + (e & 3)] : 0.f;
                 pv[e] = w;
             }
             pop[k] = u32x4{pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]),
                            pack2<F16>(pv[4], pv[5]), pack2<F16>(pv[6], pv[7])};
+            if constexpr (CHK) {
+                if (flagged)
+                    pvis[k] = u32x4{vis_pair<F16>(vis[0], vis[1]), vis_pair<F16>(vis[2], vis[3]),
+                                    vis_pair<F16>(vis[4], vis[5]), vis_pair<F16>(vis[6], vis[7])};
+            }
             if (p.dbg_visit) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -654,6 +764,22 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
             const u32x4 a = *reinterpret_cast<const u32x4*>(vt_lds + vt_off(db * 16 + ln, lg));
 #pragma unroll
             for (int k = 0; k < QB; ++k) o_acc[k][db] = mfma16x16x32<F16>(a, pop[k], o_acc[k][db]);
+        }
+        // a non-finite V value in the tile: the visible ones counted and applied
+        if constexpr (CHK) {
+            if (flagged) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const u32x4 ai = *reinterpret_cast<const u32x4*>(vt_lds + IND + vt_off(db * 16 + ln, lg));
+#pragma unroll
+                    for (int k = 0; k < QB; ++k) {
+                        const f32x4 cnt = mfma16x16x32<F16>(ai, pvis[k], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o_acc[k][db][i] = apply_nonfinite(o_acc[k][db][i], cnt[i]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);      // a rare path: one dim block at a time
+                }
+            }
         }
         if constexpr (MASK_AHEAD) {
 #pragma unroll
@@ -834,7 +960,7 @@ int resident_groups() {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_attn_kernel<MODE, KT, D, QB, W>, 64 * W,
-                                                         smem_bytes<D, MODE == kSel>()) != hipSuccess ||
+                                                         smem_bytes<D, MODE == kSel, check_v<MODE, KT>(0)>()) != hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
         cached[dev] = cus * per_cu;
@@ -844,7 +970,7 @@ int resident_groups() {
 
 template <int MODE, int KT, int D, int QB, int W>
 hipError_t launch_one(const MParams& p, dim3 grid, hipStream_t st) {
-    constexpr int smem = smem_bytes<D, MODE == kSel>();
+    constexpr int smem = smem_bytes<D, MODE == kSel, check_v<MODE, KT>(0)>();
     if constexpr (MODE == kDecode) {
         const long long items = static_cast<long long>(grid.x) * grid.y * grid.z;
         grid = dim3(decode_grid(items, resident_groups<MODE, KT, D, QB, W>()), 1, 1);
