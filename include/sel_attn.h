@@ -7,8 +7,9 @@
  * stream) and never synchronises the host.
  *
  * Ownership: the caller owns every buffer.  The library never allocates,
- * frees or keeps a pointer after a call returns; it holds no state and may be
- * called from several host threads at once.
+ * frees or keeps a pointer after a call returns.  Its only state is the
+ * scratch array of sel_attn_decode_noalloc (one per device, held until the
+ * process ends) and per-device launch settings it looks up once.
  *
  * Errors: every entry point validates its arguments on the host before any
  * HIP call and returns a negative status (nothing is launched) when they are
@@ -282,6 +283,34 @@ size_t sel_attn_args_size(int op);
  * ALU kernel, 1 = matrix-core (MFMA) kernel; negative status if invalid. */
 int sel_attn_decode_path(const sel_attn_decode_args* a);
 int sel_attn_prefill_path(const sel_attn_prefill_args* a);
+
+/*
+ * Decode and combine without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It computes exactly what sel_attn_decode followed by
+ * sel_attn_split_combine computes (same kernels), and writes the combined
+ * output out fp32 [S][R][Hq][D] (16-byte aligned), with the optional sink
+ * logits `sinks` fp32 [Hq] (device, or NULL) as in the combine.
+ *
+ * The split partials live in a scratch array of SEL_ATTN_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each device it runs on until the process ends: a
+ * call needs S * R * Hq * ceil(cap / slice_len) * (head_dim + 2) * 4 bytes of
+ * it (the 16-stream split-K and the 16 x 16-row verify workloads fit).  The
+ * call allocates and frees nothing, on the host or the device.
+ *
+ * Arguments: as sel_attn_decode, except that a->part_o and a->part_ml must be
+ * NULL and a->n_slices_max is ignored (ceil(cap / slice_len) is used).
+ * Status: EINVAL for a NULL a or out, or partial pointers given; EWORKSPACE
+ * when the partials would exceed the scratch; otherwise the statuses of
+ * sel_attn_decode and sel_attn_split_combine, checked before anything runs;
+ * EHIP if the scratch cannot be looked up on the current device.
+ * Every call on one device uses that device's one scratch array: calls that
+ * overlap on one device (two streams, two host threads) race and must be
+ * ordered by the caller.  Nothing in the scratch needs clearing between calls.
+ */
+#define SEL_ATTN_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int sel_attn_decode_noalloc(const sel_attn_decode_args* a, float* out, const float* sinks,
+                            void* hip_stream);
 
 #ifdef __cplusplus
 }

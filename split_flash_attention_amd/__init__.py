@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libselattn.so")
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 F32, F16, BF16, I8, FP8 = 0, 1, 2, 3, 4
 OP_DECODE, OP_PREFILL, OP_COMBINE = 1, 2, 3
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024     # SEL_ATTN_NOALLOC_SCRATCH_BYTES
 
 _i32, _i64, _f32, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
@@ -82,6 +83,7 @@ def lib():
                             [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t),
                              ctypes.POINTER(ctypes.c_size_t)]),
                            ("sel_attn_decode_path", [ctypes.POINTER(DecodeArgs)]),
+                           ("sel_attn_decode_noalloc", [ctypes.POINTER(DecodeArgs), _p, _p, _p]),
                            ("sel_attn_prefill_path", [ctypes.POINTER(PrefillArgs)]),
                            ("sel_attn_abi_version", []),
                            ("sel_attn_args_size", [ctypes.c_int]),
@@ -136,7 +138,8 @@ def decode_args(*, q, k, v, kv_len, part_o, part_ml, causal=True, scale, softcap
                 tree_parent=None) -> DecodeArgs:
     """Fill the decode struct from tensors: q [S][R][Hq][D] fp32 contiguous,
     k/v [S][cap][Hkv][D] (dim contiguous), scales [S][cap][Hkv], kv_len int32 [S],
-    part_o [S][R][Hq][ns][D], part_ml [S][R][Hq][ns][2], tree_parent int32 [S][R]."""
+    part_o [S][R][Hq][ns][D], part_ml [S][R][Hq][ns][2] (both None for
+    sel_attn_decode_noalloc), tree_parent int32 [S][R]."""
     S, R, Hq, D = q.shape
     a = DecodeArgs()
     a.n_stream, a.n_row, a.n_head_q, a.head_dim = S, R, Hq, D
@@ -153,7 +156,7 @@ def decode_args(*, q, k, v, kv_len, part_o, part_ml, causal=True, scale, softcap
     a.scale, a.softcap = float(scale), float(softcap)
     a.alibi_slopes = _ptr(alibi)
     a.slice_len = int(slice_len)
-    a.n_slices_max = part_o.shape[3]
+    a.n_slices_max = 0 if part_o is None else part_o.shape[3]
     a.part_o, a.part_ml, a.dbg_visit = _ptr(part_o), _ptr(part_ml), _ptr(dbg_visit)
     a.tree_parent = _ptr(tree_parent)
     return a
@@ -161,6 +164,13 @@ def decode_args(*, q, k, v, kv_len, part_o, part_ml, causal=True, scale, softcap
 
 def sel_attn_decode(args: DecodeArgs, stream=None):
     _check(lib().sel_attn_decode(ctypes.byref(args), _stream(stream)), "sel_attn_decode")
+
+
+def sel_attn_decode_noalloc(args: DecodeArgs, out, sinks=None, stream=None):
+    """Decode + combine with the partials in the library's own scratch (no
+    allocation): `args` without partial buffers, out fp32 [S][R][Hq][D]."""
+    _check(lib().sel_attn_decode_noalloc(ctypes.byref(args), _ptr(out), _ptr(sinks), _stream(stream)),
+           "sel_attn_decode_noalloc")
 
 
 def combine_args(*, part_o, part_ml, out, kv_len=None, slice_len=0, cap=0,

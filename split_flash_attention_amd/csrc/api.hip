@@ -42,6 +42,10 @@ int check_scores(float scale, float softcap) {
     return SEL_ATTN_OK;
 }
 
+}  // namespace
+
+namespace selattn {
+
 int validate_decode(const sel_attn_decode_args* a) {
     if (!a) return SEL_ATTN_EINVAL;
     if (!a->q || !a->k || !a->v || !a->kv_len || !a->part_o || !a->part_ml) return SEL_ATTN_EINVAL;
@@ -81,6 +85,13 @@ int validate_combine(const sel_attn_combine_args* a) {
         return SEL_ATTN_EUNSUPPORTED;
     return SEL_ATTN_OK;
 }
+
+}  // namespace selattn
+
+namespace {
+
+using selattn::validate_combine;
+using selattn::validate_decode;
 
 int validate_prefill(const sel_attn_prefill_args* a) {
     if (!a) return SEL_ATTN_EINVAL;

@@ -8,6 +8,10 @@
 
 namespace selattn {
 
+// Host-side argument checks of the C ABI (status codes of include/sel_attn.h).
+int validate_decode(const sel_attn_decode_args* a);
+int validate_combine(const sel_attn_combine_args* a);
+
 // Generic vector-ALU kernels (every dtype, every supported shape).
 hipError_t launch_valu_decode(const sel_attn_decode_args& a, hipStream_t st);
 hipError_t launch_valu_prefill(const sel_attn_prefill_args& a, hipStream_t st);

@@ -186,3 +186,26 @@ def test_null_struct_pointers(L):
     assert L.sel_attn_decode(None, None) == sa.EINVAL
     assert L.sel_attn_prefill(None, None) == sa.EINVAL
     assert L.sel_attn_split_combine(None, None) == sa.EINVAL
+
+
+def test_noalloc_validates_before_any_device_call(L):
+    """sel_attn_decode_noalloc refuses bad calls on the host, before it looks up its
+    scratch: partial buffers given, a NULL output, partials beyond the scratch."""
+    out = ctypes.c_void_p(FAKE)
+    a = good_decode()
+    assert L.sel_attn_decode_noalloc(ctypes.byref(a), out, None, None) == sa.EINVAL   # partials given
+    a = good_decode(part_o=None, part_ml=None)
+    assert L.sel_attn_decode_noalloc(ctypes.byref(a), None, None, None) == sa.EINVAL  # no output
+    # 16 x 16 x 48 x 64 slices x 258 x 4 B = 203 MB > the 64 MiB scratch
+    a = good_decode(part_o=None, part_ml=None, n_row=16, n_head_q=48, cap=65536)
+    assert L.sel_attn_decode_noalloc(ctypes.byref(a), out, None, None) == sa.EWORKSPACE
+    # huge sizes do not overflow the size check
+    a = good_decode(part_o=None, part_ml=None, n_stream=2 ** 31 - 1, n_row=2 ** 31 - 1,
+                    n_head_q=2 ** 31 - 1 - (2 ** 31 - 1) % 4, n_head_kv=4, slice_len=1)
+    assert L.sel_attn_decode_noalloc(ctypes.byref(a), out, None, None) == sa.EWORKSPACE
+    # a call that fits but that decode itself refuses (head_dim 96): decode's status
+    a = good_decode(part_o=None, part_ml=None, head_dim=96)
+    assert L.sel_attn_decode_noalloc(ctypes.byref(a), out, None, None) == sa.EUNSUPPORTED
+    a = good_decode(part_o=None, part_ml=None, n_head_q=30)                 # 30 % 4 != 0
+    assert L.sel_attn_decode_noalloc(ctypes.byref(a), out, None, None) == sa.EINVAL
+    assert sa.NOALLOC_SCRATCH_BYTES == 64 * 1024 * 1024
