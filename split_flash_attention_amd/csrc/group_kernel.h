@@ -571,24 +571,26 @@ inline int group_waves(int nqb) {
 template <int KT, int D, int W>
 hipError_t group_launch_one(const MParams& p, dim3 grid, hipStream_t st) {
     constexpr int smem = group_smem<D, W, KT>();
-    static int cached[16] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-    if (cached[dev] == 0) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&group_decode_kernel<KT, D, W>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-        if (e != hipSuccess) return e;
-        int cus = 0, per_cu = 0;
+    // the LDS limit is raised (per device) before the occupancy query and any launch
+    static DeviceCache cache;
+    hipError_t attr = hipSuccess;
+    const int resident = cache.get(0, [&attr]() {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&group_decode_kernel<KT, D, W>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+        if (attr != hipSuccess) return 0;
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess) dev = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, group_decode_kernel<KT, D, W>, 64 * W, smem) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
-        cached[dev] = cus * per_cu;
-    }
+        return cus * per_cu;
+    });
+    if (attr != hipSuccess) return attr;
     const long long items = static_cast<long long>(grid.x) * grid.y * grid.z;
-    hipLaunchKernelGGL((group_decode_kernel<KT, D, W>), dim3(decode_grid(items, cached[dev])), dim3(64 * W), smem,
+    hipLaunchKernelGGL((group_decode_kernel<KT, D, W>), dim3(decode_grid(items, resident)), dim3(64 * W), smem,
                        st, p);
     return hipGetLastError();
 }

@@ -652,22 +652,18 @@ __global__ __launch_bounds__(64, 2) void lean_attn_kernel(MParams p) {
 
 template <int MODE, int KT, int D, int CP, bool TREE, bool MIX>
 int lean_resident_groups(int smem) {
-    static int cached[16] = {0};
-    static int cached_smem[16] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-    if (cached[dev] == 0 || cached_smem[dev] != smem) {
-        int cus = 0, per_cu = 0;
+    static DeviceCache cache;
+    return cache.get(smem, [smem]() {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess) dev = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lean_attn_kernel<MODE, KT, D, CP, TREE, MIX>, 64, smem) !=
-                hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lean_attn_kernel<MODE, KT, D, CP, TREE, MIX>, 64,
+                                                         smem) != hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
-        cached[dev] = cus * per_cu;
-        cached_smem[dev] = smem;
-    }
-    return cached[dev];
+        return cus * per_cu;
+    });
 }
 
 template <int MODE, int KT, int D, int CP, bool TREE, bool MIX>

@@ -28,6 +28,7 @@
 
 #include "arch.h"
 #include "common.h"
+#include "device_cache.h"
 #include "internal.h"
 
 #include <algorithm>
@@ -952,20 +953,19 @@ inline Shape pick_shape(int M) {
 // Work-groups of this kernel instance that fit on the device at once (cached per device).
 template <int MODE, int KT, int D, int QB, int W>
 int resident_groups() {
-    static int cached[16] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-    if (cached[dev] == 0) {
-        int cus = 0, per_cu = 0;
+    static DeviceCache cache;
+    return cache.get(0, []() {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess) dev = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_attn_kernel<MODE, KT, D, QB, W>, 64 * W,
-                                                         smem_bytes<D, MODE == kSel, check_v<MODE, KT>(0)>()) != hipSuccess ||
+                                                         smem_bytes<D, MODE == kSel, check_v<MODE, KT>(0)>()) !=
+                hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
-        cached[dev] = cus * per_cu;
-    }
-    return cached[dev];
+        return cus * per_cu;
+    });
 }
 
 template <int MODE, int KT, int D, int QB, int W>

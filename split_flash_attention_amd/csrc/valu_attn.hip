@@ -1,4 +1,5 @@
-// Generic vector-ALU attention kernels: every storage type, every mode.
+// Generic vector-ALU attention kernels: every storage type, decode and mask-mode
+// prefill (selection mode runs on the matrix-core kernels only).
 //
 // One work-group owns up to 32 query vectors (a query vector is one (row,
 // query head) pair of one kv head) and walks a key range in tiles of 32 keys
@@ -11,6 +12,7 @@
 // attn_merge; strix-llama.cpp PR #115 split-K reduce) with NaN carried through
 // (HartsyInference PR #910, review item 1 and its fix).
 #include "common.h"
+#include "device_cache.h"
 #include "internal.h"
 
 #include <algorithm>
@@ -23,11 +25,10 @@ constexpr int kTile = 32;       // keys per tile
 constexpr int kQv = 32;         // query vectors per work-group
 constexpr int kThreads = 256;
 constexpr int kMaxD = 256;
-constexpr int kMaxSel = 4096;
 constexpr int kStageU = 8;      // K/V elements per thread in flight while staging a tile
 constexpr int kCombineRound = 8;   // partial slices per lane in flight in the combine
 
-enum Mode : int { kDecode = 0, kMask = 1, kSel = 2 };
+enum Mode : int { kDecode = 0, kMask = 1 };
 
 struct ValuParams {
     int mode;
@@ -47,11 +48,9 @@ struct ValuParams {
     const int32_t* kv_len;
     int causal;
     int slice_len, n_slices_max, n_qchunks;
-    // prefill
+    // prefill (mask mode)
     int n_kv;
     const int32_t* q_pos;
-    const int32_t* sel;
-    int n_sel, bs, sel_pow2;
     const float* mask;
     int64_t m_sr, m_sh;
     int rows_per_wg, n_splits, split_step;
@@ -60,7 +59,6 @@ struct ValuParams {
     float* part_o;
     float* part_ml;
     int64_t* dbg_visit;
-    int32_t* dbg_sel;
     const int32_t* tree;       // decode: [S][R] parent tables of tree windows, or null
     const float* sinks;        // prefill without splits: [Hq] sink logits, or null
 };
@@ -70,10 +68,7 @@ constexpr int kOffQ = 0;                                         // float [kQv][
 constexpr int kOffK = kOffQ + kQv * kMaxD * 4;                   // float [kTile][kMaxD+1]
 constexpr int kOffV = kOffK + kTile * (kMaxD + 1) * 4;           // float [kTile][kMaxD]
 constexpr int kOffP = kOffV + kTile * kMaxD * 4;                 // float [kQv][kTile]
-constexpr int kOffList = kOffP + kQv * kTile * 4;                // int [kMaxSel]
-constexpr int kSmemBytes = kOffList + kMaxSel * 4;
-// the sort buffer reuses the V tile region (sorting ends before the first tile)
-static_assert(kTile * kMaxD * 4 >= kMaxSel * 4, "sort buffer must fit in the V tile");
+constexpr int kSmemBytes = kOffP + kQv * kTile * 4;
 
 __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
     extern __shared__ __align__(16) char smem[];
@@ -81,8 +76,6 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
     float* kt = reinterpret_cast<float*>(smem + kOffK);
     float* vt = reinterpret_cast<float*>(smem + kOffV);
     float* ps = reinterpret_cast<float*>(smem + kOffP);
-    int* list = reinterpret_cast<int*>(smem + kOffList);
-    int* sortbuf = reinterpret_cast<int*>(smem + kOffV);
 
     __shared__ int cell_t[kTile];
     __shared__ uint32_t vis[kQv];
@@ -90,8 +83,6 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
     __shared__ int nan_run[kQv];
     __shared__ long long dbg[kQv][3];
     __shared__ unsigned long long tpath[kQv];     // tree windows: window nodes each query vector sees
-    __shared__ int scan[kThreads];
-    __shared__ int n_ids_s;
 
     const int tid = threadIdx.x;
     const int D = p.D;
@@ -111,14 +102,9 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
         m0 = qc * kQv;
         nq = min(kQv, p.R * G - m0);
         if (nq <= 0) return;
-    } else if (p.mode == kMask) {
+    } else {
         row0 = blockIdx.z * p.rows_per_wg;
         nq = min(p.rows_per_wg, p.R - row0) * G;
-        lo = t_split * p.split_step;
-        hi = min(lo + p.split_step, p.n_kv);
-    } else {
-        row0 = blockIdx.z;
-        nq = G;
         lo = t_split * p.split_step;
         hi = min(lo + p.split_step, p.n_kv);
     }
@@ -166,72 +152,11 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
         tpath[tid] = path;
     }
 
-    // ---- selection list: sort, drop invalid and repeated ids --------------
-    int n_slots = hi - lo;
-    if (p.mode == kSel) {
-        const int P = p.sel_pow2;
-        const int32_t* srow = p.sel + static_cast<int64_t>(row0) * p.n_sel;
-        for (int e = tid; e < P; e += kThreads) {
-            int id = 0x7fffffff;
-            if (e < p.n_sel) {
-                const int x = srow[e];
-                if (x >= 0 && static_cast<int64_t>(x) * p.bs < p.n_kv) id = x;
-            }
-            sortbuf[e] = id;
-        }
-        __syncthreads();
-        for (int k = 2; k <= P; k <<= 1) {
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                for (int e = tid; e < P; e += kThreads) {
-                    const int o = e ^ j;
-                    if (o > e) {
-                        const int x = sortbuf[e], y = sortbuf[o];
-                        const bool up = (e & k) == 0;
-                        if ((x > y) == up) { sortbuf[e] = y; sortbuf[o] = x; }
-                    }
-                }
-                __syncthreads();
-            }
-        }
-        // stable compaction of the first occurrence of each valid id
-        const int per = (P + kThreads - 1) / kThreads;
-        const int e0 = tid * per;
-        int cnt = 0;
-        for (int e = e0; e < min(e0 + per, P); ++e) {
-            const int x = sortbuf[e];
-            cnt += (x != 0x7fffffff && (e == 0 || sortbuf[e - 1] != x)) ? 1 : 0;
-        }
-        scan[tid] = cnt;
-        __syncthreads();
-        for (int off = 1; off < kThreads; off <<= 1) {
-            const int add = tid >= off ? scan[tid - off] : 0;
-            __syncthreads();
-            scan[tid] += add;
-            __syncthreads();
-        }
-        int w = scan[tid] - cnt;
-        for (int e = e0; e < min(e0 + per, P); ++e) {
-            const int x = sortbuf[e];
-            if (x != 0x7fffffff && (e == 0 || sortbuf[e - 1] != x)) list[w++] = x;
-        }
-        if (tid == kThreads - 1) n_ids_s = scan[tid];
-        __syncthreads();
-        const int n_ids = n_ids_s;
-        if (p.dbg_sel && t_split == 0) {
-            int32_t* dst = p.dbg_sel + (static_cast<int64_t>(row0) * p.Hkv + g) * (1 + p.n_sel);
-            if (tid == 0) dst[0] = n_ids;
-            for (int e = tid; e < n_ids; e += kThreads) dst[1 + e] = list[e];
-        }
-        n_slots = n_ids * p.bs;
-    }
+    const int n_slots = hi - lo;
     __syncthreads();
 
-    // cell of key slot k (-1 when the slot holds no visible key for anybody)
-    auto slot_cell = [&](int k) -> int {
-        if (p.mode != kSel) return lo + k;
-        const int c = list[k / p.bs] * p.bs + k % p.bs;
-        return (c < p.n_kv && c >= lo && c < hi) ? c : -1;
-    };
+    // cell of key slot k
+    auto slot_cell = [&](int k) -> int { return lo + k; };
     // visibility of cell c for query vector i (c >= 0)
     auto visible = [&](int i, int c) -> bool {
         if (p.mode == kDecode) {
@@ -242,13 +167,10 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
             const int lim = p.causal ? min(qpos(i) + 1, kvl) : kvl;
             return c < lim;
         }
-        if (p.mode == kMask) {
-            const float mv = p.mask[static_cast<int64_t>(qrow(i)) * p.m_sr +
-                                    static_cast<int64_t>(qhead(i)) * p.m_sh + c];
-            if (mv == kNegInf) return false;
-            return !(p.causal && c > qpos(i));
-        }
-        return true;
+        const float mv = p.mask[static_cast<int64_t>(qrow(i)) * p.m_sr +
+                                static_cast<int64_t>(qhead(i)) * p.m_sh + c];
+        if (mv == kNegInf) return false;
+        return !(p.causal && c > qpos(i));
     };
 
     const int NI = kThreads / D;                 // query-vector groups in the P.V step
@@ -562,21 +484,16 @@ __global__ __launch_bounds__(256) void combine_kernel(sel_attn_combine_args a, i
     if (sp == 0) reinterpret_cast<float4*>(out)[c] = float4{num.x / den, num.y / den, num.z / den, num.w / den};
 }
 
-int next_pow2(int x) {
-    int p = 1;
-    while (p < x) p <<= 1;
-    return p;
-}
-
+// Raises the kernel's LDS limit once per device (before its first launch there).
 hipError_t prepare_kernel() {
-    static bool done = false;
-    if (!done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&valu_attn_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
-        if (e != hipSuccess) return e;
-        done = true;
-    }
-    return hipSuccess;
+    static DeviceCache cache;
+    hipError_t err = hipSuccess;
+    cache.get(0, [&err]() {
+        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&valu_attn_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+        return err == hipSuccess ? 1 : 0;
+    });
+    return err;
 }
 
 }  // namespace
@@ -607,7 +524,7 @@ hipError_t launch_valu_prefill(const sel_attn_prefill_args& a, hipStream_t st) {
     hipError_t e = prepare_kernel();
     if (e != hipSuccess) return e;
     ValuParams p{};
-    p.mode = a.sel ? kSel : kMask;
+    p.mode = kMask;
     p.Hq = a.n_head_q; p.Hkv = a.n_head_kv; p.G = a.n_head_q / a.n_head_kv; p.D = a.head_dim;
     p.q = a.q; p.k = a.k; p.v = a.v; p.dt = a.kv_dtype;
     p.kv_sc = a.kv_stride_cell; p.kv_sh = a.kv_stride_head;
@@ -615,13 +532,12 @@ hipError_t launch_valu_prefill(const sel_attn_prefill_args& a, hipStream_t st) {
     p.sc_sc = a.sc_stride_cell; p.sc_sh = a.sc_stride_head;
     p.scale = a.scale; p.softcap = a.softcap; p.alibi = a.alibi_slopes;
     p.R = a.n_row; p.n_kv = a.n_kv; p.q_pos = a.q_pos;
-    p.sel = a.sel; p.n_sel = a.n_sel; p.bs = a.block_size; p.sel_pow2 = a.sel ? next_pow2(a.n_sel) : 0;
     p.mask = a.mask; p.m_sr = a.mask_stride_row; p.m_sh = a.mask_stride_head; p.causal = a.causal;
     p.n_splits = a.n_splits;
     p.split_step = (a.n_kv + a.n_splits - 1) / a.n_splits;
-    p.rows_per_wg = a.sel ? 1 : std::max(1, kQv / p.G);
+    p.rows_per_wg = std::max(1, kQv / p.G);
     p.out = a.out; p.part_o = a.part_o; p.part_ml = a.part_ml;
-    p.dbg_visit = a.dbg_visit; p.dbg_sel = a.dbg_sel;
+    p.dbg_visit = a.dbg_visit;
     p.sinks = a.sinks;
     const int n_rb = (a.n_row + p.rows_per_wg - 1) / p.rows_per_wg;
     dim3 grid(a.n_splits, a.n_head_kv, n_rb);
