@@ -1,6 +1,6 @@
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--verify]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 One step = one split-K decode pass of the 16-stream workload (16 streams x 1
 query row, 32/4 heads, head dim 256, bf16 K/V, depths U[1024, 32768] drawn
@@ -8,27 +8,35 @@ from seed, slices of 1024 keys): the decode kernel over every (stream, kv head,
 slice) followed by the log-sum-exp combine.  `value` is the decode K/V stream
 rate in GB/s (algorithmic bytes: every visible K and V row read once).
 
-The same run also times the maskless selected-key prefill (2048 rows at
-positions 30000..32047, 16/2 heads, head dim 256, bf16, 512 block ids per row
-over 4-cell blocks) and reports its TFLOP/s (4*D flops per visited (row, head,
-key)), the selected-key decode (16 rows, one per sequence of a unified cache, with
-the same lists and block size, the key range split 32 ways, then the combine),
-and a plain device copy of 1 GiB (the achievable copy rate, and the
-calibration for the memory counters).  Beside them: per-launch median and
-minimum times, the selected-key prefill right after a 512 MiB write (cold
-Infinity Cache), measured roofs (a bf16 8192^3 matmul, and a gather probe that
-reads exactly the K/V blocks the selected-key prefill gathers), the tiny dense
-decode and the semantic-edge mask prefill.  `--verify` adds the int8
-verify-window decode (16 streams x 16 rows, 48/4 heads, depth 32000, slices of
-2048) with chain and tree windows, and the split-K decode with e4m3 K/V rows.
+The same run times every other workload of the hot path on its own inputs,
+each with its kernel alone and with the combine that follows it, as absolute
+GB/s, TFLOP/s and tokens/s and as a fraction of its binding roof (the larger of
+bytes / 8 TB/s and flops / 2.5 PFLOP/s):
+  * the int8 verify-window decode (16 streams x 16 rows, 48/4 heads, depths
+    12000 and 32000, slices of 2048), with causal windows and with each window
+    a 16-node binary tree;
+  * the split-K decode with e4m3 K/V rows and fp32 row scales;
+  * the maskless selected-key prefill (2048 rows at positions 30000..32047,
+    16/2 heads, 512 block ids per row over 4-cell blocks; 4*D flops per visited
+    (row, head, key)) and the selected-key decode (16 rows, one per sequence of a
+    unified cache, the key range split 32 ways, then the combine);
+  * the tiny dense decode and the semantic-edge mask prefill;
+  * measured roofs: a 1 GiB device copy (also the calibration of the memory
+    counters), a bf16 8192^3 matmul, and a gather probe that reads exactly the
+    K/V blocks the selected-key prefill gathers; the selected-key prefill is
+    also timed right after a 512 MiB write (cold Infinity Cache).
+Then the FP64 oracle is timed on the host cores on bounded samples of the
+split-K decode, the selected-key prefill and the depth-32000 verify decode.
 
 Prints ONE JSON line.  Inputs are seeded synthetic data (no dataset).
 """
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -36,8 +44,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-SEL_DECODE_SPLITS = 32         # key-range splits of the selected-key decode rows (16 rows x 2 kv heads each)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+SEL_DECODE_SPLITS = 32         # key-range splits of the selected-key decode rows (16 rows x 2 kv heads each)
 
 # HBM bytes of one decode launch on the split-K workload, from two rocprofv3 --pmc
 # runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
@@ -49,7 +57,7 @@ DECODE_TRAFFIC = {"sources_sha256": "7273fdf1521d6310c25d72804953745323174e3fc50
                   "fetch_bytes": 592916.47 * 1024 * 2.0,
                   "write_bytes": 10594.20 * 1024 * 1.0}
 # the files the decode kernel is built from
-DECODE_SOURCES = ["arch.h", "common.h", "internal.h", "mfma_kernel.h", "lean_kernel.h", "mfma_decode.hip"]
+DECODE_SOURCES = ["arch.h", "common.h", "device_cache.h", "internal.h", "mfma_kernel.h", "lean_kernel.h", "mfma_decode.hip"]
 
 
 def kernel_sources_sha256():
@@ -76,7 +84,6 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--verify", action="store_true", help="also time the int8 verify-window decode")
     return ap.parse_args()
 
 
@@ -85,7 +92,8 @@ def log(msg):
 
 
 def timed(fn, steps, torch):
-    """Average ms of `fn` over `steps` back-to-back calls, HIP events on the current stream."""
+    """Average ms of `fn` over `steps` back-to-back calls, HIP events on the current
+    stream (the stream the library launches on)."""
     s = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -100,7 +108,6 @@ def timed(fn, steps, torch):
 
 def timed_each(fn, n, torch):
     """Per-call ms of `fn` over n calls (HIP events around each call): (median, min)."""
-    import statistics
     s = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
     torch.cuda.synchronize()
@@ -115,7 +122,6 @@ def timed_each(fn, n, torch):
 
 def timed_cold(fn, flush, n, torch):
     """Median ms of `fn` right after `flush` (a write larger than the Infinity Cache)."""
-    import statistics
     s = torch.cuda.current_stream()
     d = []
     for _ in range(n):
@@ -127,6 +133,69 @@ def timed_cold(fn, flush, n, torch):
         torch.cuda.synchronize()
         d.append(e0.elapsed_time(e1))
     return statistics.median(d)
+
+
+def roof_frac(nbytes, flops, ms):
+    """Fraction of the binding roof: max(bytes / HBM peak, flops / MFMA peak) / time."""
+    t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
+    return t_roof / (ms * 1e-3)
+
+
+def decode_work(wl, np):
+    """Algorithmic bytes (each visible K and V row once, row scales included) and flops
+    (4*D per visited (row, query head, key)) of a decode workload."""
+    row_bytes = wl.head_dim * (1 if wl.kv_dtype in ("i8", "fp8") else 2 if wl.kv_dtype != "f32" else 4)
+    if wl.kv_dtype in ("i8", "fp8"):
+        row_bytes += 4
+    kv_len = np.asarray(wl.kv_len, np.int64)
+    nbytes = int(kv_len.sum()) * wl.n_head_kv * row_bytes * 2
+    R = wl.n_row
+    keys = 0
+    for n in kv_len:
+        for r in range(R):
+            if wl.tree_parent is not None:
+                keys += int(n) - R + (r + 1).bit_length()          # binary heap: depth of node r + 1
+            elif wl.causal:
+                keys += int(n) - R + r + 1
+            else:
+                keys += int(n)
+    flops = 4.0 * wl.head_dim * wl.n_head_q * keys
+    return nbytes, flops
+
+
+def time_decode(name, wl, steps, sa, hip_run, torch, np, workload_text):
+    """Kernel-only and with-combine timings of one decode workload."""
+    d = hip_run.DecodeDev(wl, "cuda", poison_outputs=False)
+    a, c = d.args(), d.combine_args()
+
+    def kernel():
+        sa.sel_attn_decode(a)
+
+    def step():
+        sa.sel_attn_decode(a)
+        sa.sel_attn_split_combine(c)
+
+    step()
+    torch.cuda.synchronize()
+    ms_k = timed(kernel, steps, torch)
+    ms_s = timed(step, steps, torch)
+    k_med, k_min = timed_each(kernel, steps, torch)
+    nbytes, flops = decode_work(wl, np)
+    rows = wl.n_stream * wl.n_row
+    out = {"workload": workload_text,
+           "kernel_ms": round(ms_k, 5), "kernel_ms_median": round(k_med, 5), "kernel_ms_min": round(k_min, 5),
+           "step_ms": round(ms_s, 5),
+           "kv_bytes": nbytes, "gflop": round(flops / 1e9, 3),
+           "gbs": round(nbytes / (ms_k * 1e-3) / 1e9, 2),
+           "tflops": round(flops / (ms_k * 1e-3) / 1e12, 2),
+           "hbm_peak_frac": round(nbytes / (ms_k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "mfma_peak_frac": round(flops / (ms_k * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "binding_roof_frac": round(roof_frac(nbytes, flops, ms_k), 4),
+           "binding_roof_frac_step": round(roof_frac(nbytes, flops, ms_s), 4),
+           "tokens_per_s": round(rows / (ms_s * 1e-3), 1),
+           "decode_path": sa.decode_path(a)}
+    del d
+    return out
 
 
 def gather_roof(wl, k, v, torch, np):
@@ -170,33 +239,81 @@ def gather_roof(wl, k, v, torch, np):
     return best
 
 
-def cpu_baseline_decode(wl, min_seconds=12.0):
-    """The FP64 oracle (as it stands) on a bounded sample of the decode workload:
-    its streams one at a time, in order, until `min_seconds` have passed."""
-    import numpy as np
-    import oracle
+def sel_cells(wl, np):
+    """Visited cells of a selection workload: unique valid ids x block size, summed over rows."""
+    n = 0
+    for r in range(wl.n_row):
+        ids = wl.sel[r]
+        ok = (ids >= 0) & (ids.astype(np.int64) * wl.block_size < wl.n_kv)
+        n += np.unique(ids[ok]).size * wl.block_size
+    return n
+
+
+def host_info():
+    """The host the oracle runs on: core counts and the BLAS behind numpy."""
+    info = {"os_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        pools = threadpool_info()
+        info["blas"] = [{"api": p.get("internal_api"), "threads": p.get("num_threads"),
+                         "version": p.get("version")} for p in pools]
+        info["threads"] = max([p.get("num_threads", 1) for p in pools] + [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    cells = 0
-    n_calls = 0
+        info["threads"] = info["affinity_cpus"]
+    return info
+
+
+def cpu_baseline(wl2, wl3, wl5, np, budget_s=8.0):
+    """The FP64 oracle (as it stands) on bounded samples: the split-K decode by whole
+    streams, the selected-key prefill by rows, the verify decode by whole streams,
+    each repeated in order until `budget_s` has passed."""
+    import oracle
+    res = {}
+    # split-K decode: GB/s of K/V
+    cells = n_calls = 0
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < min_seconds:
-        b = n_calls % wl.n_stream
+    while time.perf_counter() - t0 < budget_s:
+        b = n_calls % wl2.n_stream
         sl = slice(b, b + 1)
-        oracle.decode(q=wl.q[sl], k=wl.k[sl], v=wl.v[sl], kv_dtype=wl.kv_dtype, kv_len=wl.kv_len[sl],
-                      causal=wl.causal, scale=wl.scale)
-        cells += int(wl.kv_len[b])
+        oracle.decode(q=wl2.q[sl], k=wl2.k[sl], v=wl2.v[sl], kv_dtype=wl2.kv_dtype, kv_len=wl2.kv_len[sl],
+                      causal=wl2.causal, scale=wl2.scale)
+        cells += int(wl2.kv_len[b])
         n_calls += 1
-    # (the whole workload takes about 1.4 s on 16 cores, so the sample repeats it)
     dt = time.perf_counter() - t0
-    nbytes = cells * wl.n_head_kv * wl.head_dim * 2 * 2
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"split-K decode workload: {n_calls} single-stream passes over its 16 streams "
-                      f"in order, {cells} cells x 32 query heads, {dt:.1f} s"}
+    res["split_k_decode"] = {"value": round(cells * wl2.n_head_kv * wl2.head_dim * 4 / dt / 1e9, 4),
+                             "unit": "GB/s",
+                             "sample": f"{n_calls} single-stream passes over the 16 streams in order, "
+                                       f"{cells} cells x 32 query heads, {dt:.1f} s"}
+    # selected-key prefill: TFLOP/s
+    done = flops = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        r = done % wl3.n_row
+        oracle.prefill(q=wl3.q, k=wl3.k, v=wl3.v, kv_dtype=wl3.kv_dtype, scale=wl3.scale, q_pos=wl3.q_pos,
+                       sel=wl3.sel, block_size=wl3.block_size, rows=[r])
+        ids = wl3.sel[r]
+        ok = (ids >= 0) & (ids.astype(np.int64) * wl3.block_size < wl3.n_kv)
+        flops += 4.0 * wl3.head_dim * wl3.n_head_q * np.unique(ids[ok]).size * wl3.block_size
+        done += 1
+    dt = time.perf_counter() - t0
+    res["selected_key_prefill"] = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+                                   "sample": f"{done} of the 2048 rows in order, {dt:.1f} s"}
+    # verify decode at depth 32000: TFLOP/s
+    done = 0
+    flops = 0.0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b = done % wl5.n_stream
+        sl = slice(b, b + 1)
+        oracle.decode(q=wl5.q[sl], k=wl5.k[sl], v=wl5.v[sl], kv_dtype=wl5.kv_dtype, kv_len=wl5.kv_len[sl],
+                      causal=True, scale=wl5.scale, k_scale=wl5.k_scale[sl], v_scale=wl5.v_scale[sl])
+        n = int(wl5.kv_len[b])
+        flops += sum(4.0 * wl5.head_dim * wl5.n_head_q * (n - wl5.n_row + r + 1) for r in range(wl5.n_row))
+        done += 1
+    dt = time.perf_counter() - t0
+    res["int8_verify_decode_d32000"] = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+                                        "sample": f"{done} single-stream passes (16 rows x 48 heads), {dt:.1f} s"}
+    return res
 
 
 def main():
@@ -215,24 +332,12 @@ def main():
     torch.cuda.set_device(0)
     sa.lib()
 
-    # ---- inputs (host generation, then resident in HBM) --------------------------
+    # ---- the headline workload (host generation, then resident in HBM) ----------
     log("generating the split-K decode workload")
     wl2 = gen.config2()
     d2 = hip_run.DecodeDev(wl2, "cuda", poison_outputs=False)
     a2 = d2.args()
     c2 = d2.combine_args()
-    log("generating the selected-key prefill workload")
-    wl3 = gen.config3()
-    d3 = hip_run.PrefillDev(wl3, "cuda", poison_outputs=False)
-    a3 = d3.args()
-    log("generating the selected-key decode workload")
-    wl6 = gen.sel_decode()
-    d6 = hip_run.PrefillDev(wl6, "cuda", n_splits=SEL_DECODE_SPLITS, poison_outputs=False)
-    a6 = d6.args()
-    c6 = sa.combine_args(part_o=d6.part_o, part_ml=d6.part_ml, out=d6.out.view(1, *d6.out.shape))
-    copy_src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")     # 1 GiB
-    copy_dst = torch.empty_like(copy_src)
-    copy_src.fill_(1.0)
 
     def step():
         sa.sel_attn_decode(a2)
@@ -241,92 +346,21 @@ def main():
     def decode_only():
         sa.sel_attn_decode(a2)
 
-    def prefill():
-        sa.sel_attn_prefill(a3)
-
-    def copy():
-        copy_dst.copy_(copy_src)
-
-    def sel_decode():
-        sa.sel_attn_prefill(a6)
-        sa.sel_attn_split_combine(c6)
-
     log("warmup")
     for _ in range(args.warmup):
         step()
-        prefill()
-        sel_decode()
-        copy()
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps -------------------------------------------
-    log("timing")
+    log("timing the split-K decode")
     ms_step = timed(step, args.steps, torch)
     ms_decode = timed(decode_only, args.steps, torch)
-    ms_prefill = timed(prefill, args.steps, torch)
-    ms_copy = timed(copy, max(3, args.steps // 4), torch)
-    ms_sd = timed(sel_decode, args.steps, torch)
     dec_med, dec_min = timed_each(decode_only, args.steps, torch)
-    pre_med, pre_min = timed_each(prefill, args.steps, torch)
-    sd_med, sd_min = timed_each(sel_decode, args.steps, torch)
-
-    # ---- more figures: cold selected-key prefill, measured roofs, the small workloads --
-    log("cold runs, roofs and the small workloads")
-    flush_buf = torch.empty(1 << 27, dtype=torch.float32, device="cuda")       # 512 MiB
-    ms_prefill_cold = timed_cold(prefill, lambda: flush_buf.fill_(0.5), 5, torch)
-    del flush_buf
-    gather_gbs = gather_roof(wl3, d3.k, d3.v, torch, np)
-    mm_a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16).contiguous()
-    mm_b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16).contiguous()
-    mm_c = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
-    torch.matmul(mm_a, mm_b, out=mm_c)
-    ms_mm = timed_each(lambda: torch.matmul(mm_a, mm_b, out=mm_c), 10, torch)[1]
-    matmul_tflops = 2.0 * 8192 ** 3 / (ms_mm * 1e-3) / 1e12
-    del mm_a, mm_b, mm_c
-    wl1 = gen.config1()
-    d1 = hip_run.DecodeDev(wl1, "cuda", poison_outputs=False)
-    a1, c1 = d1.args(), d1.combine_args()
-
-    def step1():
-        sa.sel_attn_decode(a1)
-        sa.sel_attn_split_combine(c1)
-
-    step1()
-    c1_med, c1_min = timed_each(step1, args.steps, torch)
-    small4 = {}
-    for name, wl4 in (("4", gen.config4()), ("4c", gen.config4(nan=False))):
-        d4 = hip_run.PrefillDev(wl4, "cuda", poison_outputs=False)
-        a4 = d4.args()
-        sa.sel_attn_prefill(a4)
-        small4[name] = timed_each(lambda: sa.sel_attn_prefill(a4), args.steps, torch)
-        del d4
 
     cells = int(np.asarray(wl2.kv_len, np.int64).sum())
     kv_bytes = cells * wl2.n_head_kv * wl2.head_dim * 2 * 2          # K and V, bf16
     gbs_step = kv_bytes / (ms_step * 1e-3) / 1e9
     gbs_kernel = kv_bytes / (ms_decode * 1e-3) / 1e9
-
-    # selected-key prefill work: 4*D flops per visited (row, query head, key)
-    n_cells = 0
-    for r in range(wl3.n_row):
-        ids = wl3.sel[r]
-        ok = (ids >= 0) & (ids.astype(np.int64) * wl3.block_size < wl3.n_kv)
-        n_cells += np.unique(ids[ok]).size * wl3.block_size
-    flops3 = 4.0 * wl3.head_dim * wl3.n_head_q * n_cells
-    gather3 = n_cells * wl3.n_head_kv * wl3.head_dim * 2 * 2
-    tflops3 = flops3 / (ms_prefill * 1e-3) / 1e12
-
-    def sel_cells(wl):
-        n = 0
-        for r in range(wl.n_row):
-            ids = wl.sel[r]
-            ok = (ids >= 0) & (ids.astype(np.int64) * wl.block_size < wl.n_kv)
-            n += np.unique(ids[ok]).size * wl.block_size
-        return n
-
-    cells6 = sel_cells(wl6)
-    flops6 = 4.0 * wl6.head_dim * wl6.n_head_q * cells6
-    gather6 = cells6 * wl6.n_head_kv * wl6.head_dim * 2 * 2
 
     result = {
         "metric": "decode KV GB/s (% HBM peak) + sel-prefill TFLOP/s, GQA h256 at 32k depth",
@@ -348,126 +382,150 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs_kernel, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs_kernel / HBM_PEAK_GBS, 4),
                      "traffic": decode_traffic(),
-                     "kernel": "decode (lean_attn_kernel<0, 2, 256>: decode, bf16, D=256)",
+                     "kernel": "decode (lean_attn_kernel<0, 2, 256, 2, false, false>: decode, bf16, D=256)",
                      "kernel_ms": round(ms_decode, 5),
                      "kernel_ms_median": round(dec_med, 5), "kernel_ms_min": round(dec_min, 5)},
-        "sel_prefill": {"workload": "2048 rows x 512 block ids (4-cell blocks), 16/2 heads, D=256, bf16",
-                        "ms": round(ms_prefill, 5), "ms_median": round(pre_med, 5),
-                        "ms_min": round(pre_min, 5), "ms_cold": round(ms_prefill_cold, 5),
-                        "tflops": round(tflops3, 3),
-                        "mfma_peak_frac": round(tflops3 / BF16_PEAK_TFLOPS, 5),
-                        "gathered_gbs": round(gather3 / (ms_prefill * 1e-3) / 1e9, 2),
-                        "gather_roof_gbs": round(gather_gbs, 1),
-                        "gather_roof_frac": round(gather3 / (ms_prefill * 1e-3) / 1e9 / gather_gbs, 4),
-                        "tokens_per_s": round(wl3.n_row / (ms_prefill * 1e-3), 1),
-                        "prefill_path": sa.prefill_path(a3)},
-        "sel_decode": {"workload": f"16 rows x 512 block ids (4-cell blocks), 16/2 heads, D=256, bf16, "
-                                   f"N=32048, {SEL_DECODE_SPLITS} key-range splits + combine",
-                       "ms": round(ms_sd, 5), "ms_median": round(sd_med, 5), "ms_min": round(sd_min, 5),
-                       "tflops": round(flops6 / (ms_sd * 1e-3) / 1e12, 3),
-                       "gathered_gbs": round(gather6 / (ms_sd * 1e-3) / 1e9, 2),
-                       "tokens_per_s": round(wl6.n_row / (ms_sd * 1e-3), 1)},
-        "dense_decode_tiny": {"workload": "1 row, 4/1 heads, D=256, 64 fp32 keys, decode + combine",
-                              "us_median": round(c1_med * 1e3, 2), "us_min": round(c1_min * 1e3, 2)},
-        "semantic_edge_prefill": {"workload": "256 rows x 4096 keys, 16/4 heads, D=128, fp16, softcap, "
-                                              "ALiBi, F32 mask (with NaN K / control without)",
-                                  "us_median": round(small4["4"][0] * 1e3, 2),
-                                  "us_median_control": round(small4["4c"][0] * 1e3, 2)},
-        "roofs": {"hbm_peak_gbs": HBM_PEAK_GBS, "bf16_mfma_peak_tflops": BF16_PEAK_TFLOPS,
-                  "copy_gbs": round(2 * copy_src.numel() * 4 / (ms_copy * 1e-3) / 1e9, 1),
-                  "bf16_matmul_tflops": round(matmul_tflops, 1),
-                  "sel_gather_gbs": round(gather_gbs, 1)},
-        "copy_gbs": round(2 * copy_src.numel() * 4 / (ms_copy * 1e-3) / 1e9, 1),
         "tokens_per_s": round(wl2.n_stream / (ms_step * 1e-3), 1),
     }
 
-    if args.verify:
-        log("generating the int8 verify-window workload at depth 12000")
-        wl5a = gen.config5(12000)
-        d5a = hip_run.DecodeDev(wl5a, "cuda", poison_outputs=False)
-        a5a, c5a = d5a.args(), d5a.combine_args()
+    # ---- the other decode workloads ----------------------------------------------
+    log("generating and timing the int8 verify-window decode at depth 12000")
+    wl5a = gen.config5(12000)
+    result["verify_decode_d12000"] = time_decode(
+        "5a", wl5a, args.steps, sa, hip_run, torch, np,
+        "int8 verify: 16 streams x 16-row causal windows, 48/4 heads, D=256, depth 12000, slices of 2048")
+    del wl5a
+    log("generating and timing the int8 verify-window decode at depth 32000 (chain and tree windows)")
+    wl5 = gen.config5(32000)
+    result["verify_decode_d32000"] = time_decode(
+        "5b", wl5, args.steps, sa, hip_run, torch, np,
+        "int8 verify: 16 streams x 16-row causal windows, 48/4 heads, D=256, depth 32000, slices of 2048")
+    wl5t = dataclasses.replace(wl5, tree_parent=np.tile(gen.heap_parents(16), (16, 1)).astype(np.int32),
+                               name="int8_tree_verify_decode_d32000")
+    result["tree_verify_decode_d32000"] = time_decode(
+        "5t", wl5t, args.steps, sa, hip_run, torch, np,
+        "int8 verify as at depth 32000, each window a 16-node binary tree in heap order")
+    del wl5t
+    log("generating and timing the split-K decode with e4m3 K/V")
+    wl2f = gen.config2(kv_dtype="fp8")
+    result["fp8_decode"] = time_decode(
+        "2f", wl2f, args.steps, sa, hip_run, torch, np,
+        "split-K decode as the headline with e4m3 K/V rows + fp32 row scales")
+    del wl2f
 
-        def step5a():
-            sa.sel_attn_decode(a5a)
-            sa.sel_attn_split_combine(c5a)
+    # ---- selected-key prefill and decode ------------------------------------------
+    log("generating the selected-key workloads")
+    wl3 = gen.config3()
+    d3 = hip_run.PrefillDev(wl3, "cuda", poison_outputs=False)
+    a3 = d3.args()
+    wl6 = gen.sel_decode()
+    d6 = hip_run.PrefillDev(wl6, "cuda", n_splits=SEL_DECODE_SPLITS, poison_outputs=False)
+    a6 = d6.args()
+    c6 = sa.combine_args(part_o=d6.part_o, part_ml=d6.part_ml, out=d6.out.view(1, *d6.out.shape))
 
-        step5a()
-        ms5a = timed(step5a, args.steps, torch)
-        bytes5a = int(np.asarray(wl5a.kv_len, np.int64).sum()) * wl5a.n_head_kv * (wl5a.head_dim + 4) * 2
-        flops5a = sum(4.0 * wl5a.head_dim * wl5a.n_head_q * wl5a.n_stream * (int(wl5a.kv_len[0]) - wl5a.n_row + r + 1)
-                      for r in range(wl5a.n_row))
-        result["verify_decode_d12000"] = {"workload": "int8 verify: 16 streams x 16 rows, 48/4 heads, D=256, depth 12000",
-                                          "ms": round(ms5a, 5), "gbs": round(bytes5a / (ms5a * 1e-3) / 1e9, 2),
-                                          "tflops": round(flops5a / (ms5a * 1e-3) / 1e12, 2),
-                                          "tokens_per_s": round(wl5a.n_stream * wl5a.n_row / (ms5a * 1e-3), 1)}
-        del d5a
-        log("generating the int8 verify-window workload at depth 32000")
-        wl5 = gen.config5(32000)
-        d5 = hip_run.DecodeDev(wl5, "cuda", poison_outputs=False)
-        a5, c5 = d5.args(), d5.combine_args()
+    def prefill():
+        sa.sel_attn_prefill(a3)
 
-        def step5():
-            sa.sel_attn_decode(a5)
-            sa.sel_attn_split_combine(c5)
+    def sel_decode():
+        sa.sel_attn_prefill(a6)
+        sa.sel_attn_split_combine(c6)
 
-        step5()
-        ms5 = timed(step5, args.steps, torch)
-        cells5 = int(np.asarray(wl5.kv_len, np.int64).sum())
-        bytes5 = cells5 * wl5.n_head_kv * (wl5.head_dim + 4) * 2
-        flops5 = 0.0
-        for r in range(wl5.n_row):
-            flops5 += 4.0 * wl5.head_dim * wl5.n_head_q * wl5.n_stream * (int(wl5.kv_len[0]) - wl5.n_row + r + 1)
-        roof5 = max(bytes5 / (HBM_PEAK_GBS * 1e9), flops5 / (BF16_PEAK_TFLOPS * 1e12)) * 1e3   # ms
-        result["verify_decode"] = {"workload": "int8 verify: 16 streams x 16 rows, 48/4 heads, D=256, depth 32000",
-                                   "ms": round(ms5, 5), "gbs": round(bytes5 / (ms5 * 1e-3) / 1e9, 2),
-                                   "hbm_peak_frac": round(bytes5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                   "tflops": round(flops5 / (ms5 * 1e-3) / 1e12, 2),
-                                   "mfma_peak_frac": round(flops5 / (ms5 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                                   "binding_roof_frac": round(roof5 / ms5, 4),
-                                   "tokens_per_s": round(wl5.n_stream * wl5.n_row / (ms5 * 1e-3), 1)}
-        del d5
-        log("generating the int8 tree verify-window workload")
-        wl5t = gen.config5(32000, tree="heap")
-        d5t = hip_run.DecodeDev(wl5t, "cuda", poison_outputs=False)
-        a5t, c5t = d5t.args(), d5t.combine_args()
+    def sel_decode_kernel():
+        sa.sel_attn_prefill(a6)
 
-        def step5t():
-            sa.sel_attn_decode(a5t)
-            sa.sel_attn_split_combine(c5t)
+    log("timing the selected-key workloads")
+    for _ in range(args.warmup):
+        prefill()
+        sel_decode()
+    ms_prefill = timed(prefill, args.steps, torch)
+    pre_med, pre_min = timed_each(prefill, args.steps, torch)
+    ms_sd = timed(sel_decode, args.steps, torch)
+    ms_sdk = timed(sel_decode_kernel, args.steps, torch)
+    sd_med, sd_min = timed_each(sel_decode, args.steps, torch)
+    flush_buf = torch.empty(1 << 27, dtype=torch.float32, device="cuda")       # 512 MiB
+    ms_prefill_cold = timed_cold(prefill, lambda: flush_buf.fill_(0.5), 5, torch)
+    del flush_buf
+    gather_gbs = gather_roof(wl3, d3.k, d3.v, torch, np)
+    n_cells = sel_cells(wl3, np)
+    flops3 = 4.0 * wl3.head_dim * wl3.n_head_q * n_cells
+    gather3 = n_cells * wl3.n_head_kv * wl3.head_dim * 2 * 2
+    tflops3 = flops3 / (ms_prefill * 1e-3) / 1e12
+    result["sel_prefill"] = {"workload": "2048 rows x 512 block ids (4-cell blocks), 16/2 heads, D=256, bf16",
+                             "ms": round(ms_prefill, 5), "ms_median": round(pre_med, 5),
+                             "ms_min": round(pre_min, 5), "ms_cold": round(ms_prefill_cold, 5),
+                             "gflop": round(flops3 / 1e9, 3),
+                             "tflops": round(tflops3, 3),
+                             "mfma_peak_frac": round(tflops3 / BF16_PEAK_TFLOPS, 5),
+                             "gathered_gbs": round(gather3 / (ms_prefill * 1e-3) / 1e9, 2),
+                             "gather_roof_gbs": round(gather_gbs, 1),
+                             "gather_roof_frac": round(gather3 / (ms_prefill * 1e-3) / 1e9 / gather_gbs, 4),
+                             "tokens_per_s": round(wl3.n_row / (ms_prefill * 1e-3), 1),
+                             "prefill_path": sa.prefill_path(a3)}
+    cells6 = sel_cells(wl6, np)
+    flops6 = 4.0 * wl6.head_dim * wl6.n_head_q * cells6
+    gather6 = cells6 * wl6.n_head_kv * wl6.head_dim * 2 * 2
+    result["sel_decode"] = {"workload": f"16 rows x 512 block ids (4-cell blocks), 16/2 heads, D=256, bf16, "
+                                        f"N=32048, {SEL_DECODE_SPLITS} key-range splits + combine",
+                            "kernel_ms": round(ms_sdk, 5), "step_ms": round(ms_sd, 5),
+                            "step_ms_median": round(sd_med, 5), "step_ms_min": round(sd_min, 5),
+                            "tflops": round(flops6 / (ms_sd * 1e-3) / 1e12, 3),
+                            "gathered_gbs": round(gather6 / (ms_sd * 1e-3) / 1e9, 2),
+                            "tokens_per_s": round(wl6.n_row / (ms_sd * 1e-3), 1)}
+    del d6
 
-        step5t()
-        ms5t = timed(step5t, args.steps, torch)
-        # visible keys of heap node r: the cached prefix plus floor(log2(r + 1)) + 1 window nodes
-        flops5t = 0.0
-        for r in range(wl5t.n_row):
-            vis = int(wl5t.kv_len[0]) - wl5t.n_row + (r + 1).bit_length()
-            flops5t += 4.0 * wl5t.head_dim * wl5t.n_head_q * wl5t.n_stream * vis
-        result["tree_verify_decode"] = {"workload": "int8 verify as above, each window a 16-node binary "
-                                                    "tree in heap order",
-                                        "ms": round(ms5t, 5), "gbs": round(bytes5 / (ms5t * 1e-3) / 1e9, 2),
-                                        "tflops": round(flops5t / (ms5t * 1e-3) / 1e12, 2)}
-        del d5t
-        log("generating the split-K decode workload with e4m3 K/V")
-        wl2f = gen.config2(kv_dtype="fp8")
-        d2f = hip_run.DecodeDev(wl2f, "cuda", poison_outputs=False)
-        a2f, c2f = d2f.args(), d2f.combine_args()
+    # ---- small workloads and measured roofs ---------------------------------------
+    log("small workloads and roofs")
+    wl1 = gen.config1()
+    d1 = hip_run.DecodeDev(wl1, "cuda", poison_outputs=False)
+    a1, c1 = d1.args(), d1.combine_args()
 
-        def step2f():
-            sa.sel_attn_decode(a2f)
-            sa.sel_attn_split_combine(c2f)
+    def step1():
+        sa.sel_attn_decode(a1)
+        sa.sel_attn_split_combine(c1)
 
-        step2f()
-        ms2f = timed(step2f, args.steps, torch)
-        bytes2f = cells * wl2f.n_head_kv * (wl2f.head_dim + 4) * 2         # e4m3 rows + fp32 scales
-        result["fp8_decode"] = {"workload": "split-K decode as above with e4m3 K/V rows + fp32 row scales",
-                                "ms": round(ms2f, 5), "gbs": round(bytes2f / (ms2f * 1e-3) / 1e9, 2),
-                                "hbm_peak_frac": round(bytes2f / (ms2f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                "tokens_per_s": round(wl2f.n_stream / (ms2f * 1e-3), 1)}
-        del d2f
+    step1()
+    c1_med, c1_min = timed_each(step1, args.steps, torch)
+    result["dense_decode_tiny"] = {"workload": "1 row, 4/1 heads, D=256, 64 fp32 keys, decode + combine",
+                                   "us_median": round(c1_med * 1e3, 2), "us_min": round(c1_min * 1e3, 2)}
+    small4 = {}
+    for name, wl4 in (("4", gen.config4()), ("4c", gen.config4(nan=False))):
+        d4 = hip_run.PrefillDev(wl4, "cuda", poison_outputs=False)
+        a4 = d4.args()
+        sa.sel_attn_prefill(a4)
+        small4[name] = timed_each(lambda: sa.sel_attn_prefill(a4), args.steps, torch)
+        del d4
+    result["semantic_edge_prefill"] = {"workload": "256 rows x 4096 keys, 16/4 heads, D=128, fp16, softcap, "
+                                                   "ALiBi, F32 mask (with NaN K / control without)",
+                                       "us_median": round(small4["4"][0] * 1e3, 2),
+                                       "us_median_control": round(small4["4c"][0] * 1e3, 2)}
+    copy_src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")     # 1 GiB
+    copy_dst = torch.empty_like(copy_src)
+    copy_src.fill_(1.0)
+    copy_dst.copy_(copy_src)
+    ms_copy = timed(lambda: copy_dst.copy_(copy_src), max(3, args.steps // 4), torch)
+    del copy_src, copy_dst
+    mm_a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16).contiguous()
+    mm_b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16).contiguous()
+    mm_c = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    torch.matmul(mm_a, mm_b, out=mm_c)
+    ms_mm = timed_each(lambda: torch.matmul(mm_a, mm_b, out=mm_c), 10, torch)[1]
+    del mm_a, mm_b, mm_c
+    copy_gbs = 2 * (1 << 28) * 4 / (ms_copy * 1e-3) / 1e9
+    result["roofs"] = {"hbm_peak_gbs": HBM_PEAK_GBS, "bf16_mfma_peak_tflops": BF16_PEAK_TFLOPS,
+                       "copy_gbs": round(copy_gbs, 1),
+                       "bf16_matmul_tflops": round(2.0 * 8192 ** 3 / (ms_mm * 1e-3) / 1e12, 1),
+                       "sel_gather_gbs": round(gather_gbs, 1)}
+    result["copy_gbs"] = round(copy_gbs, 1)
 
     if not args.no_cpu_baseline:
-        log("timing the FP64 oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline_decode(wl2)
+        log("timing the FP64 oracle on samples")
+        info = host_info()
+        cb = cpu_baseline(wl2, wl3, wl5, np)
+        head = cb["split_k_decode"]
+        result["cpu_baseline"] = {"value": head["value"], "unit": head["unit"], "cores": int(info["threads"]),
+                                  "kind": "oracle", "sample": "split-K decode workload: " + head["sample"],
+                                  "others": {k: v for k, v in cb.items() if k != "split_k_decode"},
+                                  "host": info}
 
     print(json.dumps(result), flush=True)
 

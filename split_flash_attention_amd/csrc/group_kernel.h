@@ -197,8 +197,12 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
             }
         }
     };
-    // chk: the tile is seen in part by some query vector, so its V is checked
-    auto store_tile = [&](const Regs& rg, bool chk) __attribute__((always_inline)) {
+    // tile t0 is seen in full by every query vector of the work-group
+    auto full_tile = [&](int t0) -> bool { return t0 + kTK <= n_full; };
+    // mode 0: plain; 1: plain, and the V words are checked for Inf / NaN (a tile some
+    // query vector sees in part); 2: V split into its finite part and indicator (the
+    // second staging of a checked tile that held one)
+    auto store_tile = [&](const Regs& rg, int mode) __attribute__((always_inline)) {
         uint32_t nfa = 0u;
 #pragma unroll
         for (int i = 0; i < NSLOT; ++i) {
@@ -246,9 +250,9 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                             uint32_t lo_e, lo_o, hi_e, hi_o;
                             vpairs_bf16<KT>(w[0][h], w[1][h], jj >> 1, lo_e, lo_o);
                             vpairs_bf16<KT>(w[2][h], w[3][h], jj >> 1, hi_e, hi_o);
-                            if (CHK && chk) {
-                                nfa = store_v_checked<F16>(vt_lds + (wbc ^ (jj << 6)), ind_off, lo_e, hi_e, nfa);
-                                nfa = store_v_checked<F16>(vt_lds + (wbc ^ ((jj + 1) << 6)), ind_off, lo_o, hi_o, nfa);
+                            if (CHK && mode != 0) {
+                                nfa = store_v<F16>(vt_lds + (wbc ^ (jj << 6)), ind_off, lo_e, hi_e, mode == 2, nfa);
+                                nfa = store_v<F16>(vt_lds + (wbc ^ ((jj + 1) << 6)), ind_off, lo_o, hi_o, mode == 2, nfa);
                             } else {
                                 *reinterpret_cast<uint2*>(vt_lds + (wbc ^ (jj << 6))) = uint2{lo_e, hi_e};
                                 *reinterpret_cast<uint2*>(vt_lds + (wbc ^ ((jj + 1) << 6))) = uint2{lo_o, hi_o};
@@ -269,7 +273,7 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
                             hi2 = (w[2][wi] & 0xffffu) | (w[3][wi] << 16);
                         }
                     }
-                    if (CHK && chk) nfa = store_v_checked<F16>(vt_lds + vt_off(hc * EPH + dd, gq) + 8 * kb, ind_off, lo2, hi2, nfa);
+                    if (CHK && mode != 0) nfa = store_v<F16>(vt_lds + vt_off(hc * EPH + dd, gq) + 8 * kb, ind_off, lo2, hi2, mode == 2, nfa);
                     else *reinterpret_cast<uint2*>(vt_lds + vt_off(hc * EPH + dd, gq) + 8 * kb) = uint2{lo2, hi2};
                 }
                 }
@@ -282,14 +286,28 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
             }
         }
         if constexpr (CHK) {
-            if (chk) {                              // uniform
-                const bool any = wave_any(nfa != 0u);
+            if (mode == 1) {                        // uniform
+                const bool any = wave_any(nonfinite_found(nfa));
                 if (lane == 0) wflag[wave] = any ? 1u : 0u;
             }
         }
     };
-    // tile t0 is seen in full by every query vector of the work-group
-    auto full_tile = [&](int t0) -> bool { return t0 + kTK <= n_full; };
+    // Stages tile t0 from rg; a tile some query vector sees in part is checked, and
+    // staged again split if any wave found an Inf or NaN.  Returns that finding
+    // (uniform).  Ends with a barrier: the tile is ready for every wave.
+    auto stage = [&](const Regs& rg, int t0) __attribute__((always_inline)) -> bool {
+        const bool chk = CHK && !full_tile(t0);
+        store_tile(rg, chk ? 1 : 0);
+        __syncthreads();
+        if (!chk) return false;
+        uint32_t f = 0u;
+#pragma unroll
+        for (int w = 0; w < W; ++w) f |= wflag[w];
+        if (f == 0u) return false;
+        store_tile(rg, 2);
+        __syncthreads();
+        return true;
+    };
 
 
     // ---- running state ---------------------------------------------------------
@@ -318,8 +336,9 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         vread[par] = (ln ^ x) * 64 + ((lg ^ ((ln >> 2) & 3)) << 4);
     }
 
-    // one tile of math on the staged K/V (the caller brackets it with barriers)
-    auto tile_math = [&](int t0) __attribute__((always_inline)) {
+    // one tile of math on the staged K/V (the caller brackets it with barriers);
+    // flagged: the tile's V held an Inf or NaN and was staged split
+    auto tile_math = [&](int t0, bool flagged) __attribute__((always_inline)) {
         f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
@@ -451,24 +470,19 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         // product above used its finite part; the visible non-finite values are
         // counted from the indicator tile and applied
         if constexpr (CHK) {
-            if (!full) {
-                uint32_t f = 0u;
+            if (flagged) {
+                bool vis[8];
 #pragma unroll
-                for (int w = 0; w < W; ++w) f |= wflag[w];
-                if (f != 0u) {
-                    bool vis[8];
+                for (int e = 0; e < 8; ++e) vis[e] = (vword >> ((e >> 2) * 16 + (e & 3))) & 1u;
+                const u32x4 pvis = u32x4{vis_pair<F16>(vis[0], vis[1]), vis_pair<F16>(vis[2], vis[3]),
+                                         vis_pair<F16>(vis[4], vis[5]), vis_pair<F16>(vis[6], vis[7])};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) vis[e] = (vword >> ((e >> 2) * 16 + (e & 3))) & 1u;
-                    const u32x4 pvis = u32x4{vis_pair<F16>(vis[0], vis[1]), vis_pair<F16>(vis[2], vis[3]),
-                                             vis_pair<F16>(vis[4], vis[5]), vis_pair<F16>(vis[6], vis[7])};
+                for (int db = 0; db < NDB; ++db) {
+                    const u32x4 ai = *reinterpret_cast<const u32x4*>(vt_lds + ind_off + vread[db & 1] + db * 1024);
+                    const f32x4 cnt = mfma16x16x32<F16>(ai, pvis, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const u32x4 ai = *reinterpret_cast<const u32x4*>(vt_lds + ind_off + vread[db & 1] + db * 1024);
-                        const f32x4 cnt = mfma16x16x32<F16>(ai, pvis, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) o_acc[db][i] = apply_nonfinite(o_acc[db][i], cnt[i]);
-                        __builtin_amdgcn_sched_barrier(0);      // a rare path: one dim block at a time
-                    }
+                    for (int i = 0; i < 4; ++i) o_acc[db][i] = apply_nonfinite(o_acc[db][i], cnt[i]);
+                    __builtin_amdgcn_sched_barrier(0);      // a rare path: one dim block at a time
                 }
             }
         }
@@ -480,16 +494,14 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         if (n_keys > 0) load_tile(ra, 0);
         if (n_keys > kTK) load_tile(rb, kTK);
         for (int t0 = 0; t0 < n_keys; t0 += 2 * kTK) {
-            store_tile(ra, !full_tile(t0));
-            __syncthreads();
+            const bool fa = stage(ra, t0);
             if (t0 + 2 * kTK < n_keys) load_tile(ra, t0 + 2 * kTK);
-            if (wave_live) tile_math(t0);
+            if (wave_live) tile_math(t0, fa);
             __syncthreads();
             if (t0 + kTK < n_keys) {
-                store_tile(rb, !full_tile(t0 + kTK));
-                __syncthreads();
+                const bool fb = stage(rb, t0 + kTK);
                 if (t0 + 3 * kTK < n_keys) load_tile(rb, t0 + 3 * kTK);
-                if (wave_live) tile_math(t0 + kTK);
+                if (wave_live) tile_math(t0 + kTK, fb);
                 __syncthreads();
             }
         }
@@ -499,10 +511,9 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
         Regs ra;
         if (n_keys > 0) load_tile(ra, 0);
         for (int t0 = 0; t0 < n_keys; t0 += kTK) {
-            store_tile(ra, !full_tile(t0));
-            __syncthreads();
+            const bool fa = stage(ra, t0);
             if (t0 + kTK < n_keys) load_tile(ra, t0 + kTK);
-            if (wave_live) tile_math(t0);
+            if (wave_live) tile_math(t0, fa);
             __syncthreads();
         }
     }

@@ -355,9 +355,11 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
             }
         }
     };
-    // chk: the tile is seen in part by some query vector, so its V is checked;
-    // returns (wave-uniform) whether a non-finite V value was staged
-    auto store_tile = [&](bool chk) -> bool {
+    // mode 0: plain; 1: plain, and the V words are checked for Inf / NaN (a tile some
+    // query vector sees in part); 2: V split into its finite part and indicator (the
+    // second staging of a checked tile that held one).  Returns (wave-uniform) whether
+    // a checked tile held one.
+    auto store_tile = [&](int mode) -> bool {
         uint32_t nfa = 0u;
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
@@ -394,9 +396,9 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                         uint32_t lo_e, lo_o, hi_e, hi_o;
                         vpairs_bf16<KT>(vreg[i][0][w], vreg[i][1][w], h, lo_e, lo_o);
                         vpairs_bf16<KT>(vreg[i][2][w], vreg[i][3][w], h, hi_e, hi_o);
-                        if (CHK && chk) {
-                            nfa = store_v_checked<F16>(vt_lds + vt16_off(ch * EPC + dd, kg), IND, lo_e, hi_e, nfa);
-                            nfa = store_v_checked<F16>(vt_lds + vt16_off(ch * EPC + dd + 1, kg), IND, lo_o, hi_o, nfa);
+                        if (CHK && mode != 0) {
+                            nfa = store_v<F16>(vt_lds + vt16_off(ch * EPC + dd, kg), IND, lo_e, hi_e, mode == 2, nfa);
+                            nfa = store_v<F16>(vt_lds + vt16_off(ch * EPC + dd + 1, kg), IND, lo_o, hi_o, mode == 2, nfa);
                         } else {
                             *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd, kg)) = uint2{lo_e, hi_e};
                             *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd + 1, kg)) = uint2{lo_o, hi_o};
@@ -414,7 +416,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                             lo2 = (vreg[i][0][w] & 0xffffu) | (vreg[i][1][w] << 16);
                             hi2 = (vreg[i][2][w] & 0xffffu) | (vreg[i][3][w] << 16);
                         }
-                        if (CHK && chk) nfa = store_v_checked<F16>(vt_lds + vt16_off(ch * EPC + dd, kg), IND, lo2, hi2, nfa);
+                        if (CHK && mode != 0) nfa = store_v<F16>(vt_lds + vt16_off(ch * EPC + dd, kg), IND, lo2, hi2, mode == 2, nfa);
                         else *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd, kg)) = uint2{lo2, hi2};
                     }
                 }
@@ -426,7 +428,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                 vsc_lds[lane] = vscr;
             }
         }
-        if constexpr (CHK) return chk && wave_any(nfa != 0u);
+        if constexpr (CHK) return mode == 1 && wave_any(nonfinite_found(nfa));
         return false;
     };
 
@@ -461,7 +463,8 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     for (int t0 = 0; t0 < n_keys; t0 += kLT) {
         // uniform: every query vector sees the whole tile
         const bool full = (MODE == kDecode) && t0 + kLT <= n_full;
-        const bool flagged = store_tile(!full);
+        const bool flagged = store_tile(CHK && !full ? 1 : 0);
+        if (flagged) store_tile(2);                    // the registers still hold the tile
         if (t0 + kLT < n_keys) fill_cells(t0 + kLT);
         __syncthreads();
         if (t0 + kLT < n_keys) load_tile(t0 + kLT);

@@ -211,16 +211,28 @@ __device__ __forceinline__ int vt_off(int d, int cc) {
 // such a key a zero weight for the query vectors that exclude it, and 0 * NaN or
 // 0 * Inf is NaN: a non-finite V value would leak into outputs that must never
 // read it (strix-llama.cpp PR #115, "Measurements": with poison=1 the masked cells
-// are skipped, not weighted with zero).  In a tile whose visibility differs
-// between the query vectors, staging therefore writes V^T with every Inf / NaN
-// half replaced by +0 (the product over it is the finite part, exact) and, beside
-// it, an indicator tile of the same layout: 1 for NaN, 64 for +Inf, 4096 for -Inf.
-// When a tile held a non-finite value, the indicator tile times the visibility of
-// each key (1 or 0) counts, per output, the visible NaN, +Inf and -Inf values, and
-// those counts turn the output into NaN or +-Inf as the sum over the visible keys
-// would.  Tiles every query vector sees in full, and int8 data (always finite),
-// are staged as they are.
+// are skipped, not weighted with zero).  Staging a tile whose visibility differs
+// between the query vectors therefore also checks its V words for an all-ones
+// exponent.  A tile that held an Inf or NaN is staged once more, before its
+// registers are reused: V^T with every Inf / NaN half replaced by +0 (the product
+// over it is the finite part, exact) and, beside it, an indicator tile of the same
+// layout: 1 for NaN, 64 for +Inf, 4096 for -Inf.  The indicator tile times the
+// visibility of each key (1 or 0) then counts, per output, the visible NaN, +Inf
+// and -Inf values, and those counts turn the output into NaN or +-Inf as the sum
+// over the visible keys would.  Tiles every query vector sees in full, and int8
+// data (always finite), are staged as they are.
 // ---------------------------------------------------------------------------
+
+// Accumulates, for a word of two packed 16-bit values, a term whose bit 15 or 31
+// ends up set iff that half has an all-ones exponent (Inf or NaN): the masked
+// exponent plus its lowest bit carries into the sign position only then.
+template <bool F16>
+__device__ __forceinline__ uint32_t nonfinite_acc(uint32_t acc, uint32_t w) {
+    constexpr uint32_t M = F16 ? 0x7C007C00u : 0x7F807F80u;
+    constexpr uint32_t C = F16 ? 0x04000400u : 0x00800080u;
+    return acc | ((w & M) + C);
+}
+__device__ __forceinline__ bool nonfinite_found(uint32_t acc) { return (acc & 0x80008000u) != 0u; }
 
 // Splits a word of two packed 16-bit V values into its finite part (Inf and NaN
 // halves replaced by +0) and the indicator of its non-finite halves (1 for NaN, 64
@@ -268,16 +280,21 @@ __device__ __forceinline__ float apply_nonfinite(float o, float cnt) {
     return o + add;
 }
 
-// Stores one V^T word of a tile that is seen in part: the finite part at `at`, the
-// indicator at `at + ind_off`; returns `nfa` with the indicator OR-ed in.
+// Stores one V^T word pair: plainly (split = false; the pair is checked into nfa),
+// or split into its finite part at `at` and its indicator at `at + ind_off`.
 template <bool F16>
-__device__ __forceinline__ uint32_t store_v_checked(char* at, int ind_off, uint32_t lo, uint32_t hi, uint32_t nfa) {
+__device__ __forceinline__ uint32_t store_v(char* at, int ind_off, uint32_t lo, uint32_t hi, bool split,
+                                            uint32_t nfa) {
+    if (!split) {
+        *reinterpret_cast<uint2*>(at) = uint2{lo, hi};
+        return nonfinite_acc<F16>(nonfinite_acc<F16>(nfa, lo), hi);
+    }
     uint32_t flo, ilo, fhi, ihi;
     split_nonfinite<F16>(lo, flo, ilo);
     split_nonfinite<F16>(hi, fhi, ihi);
     *reinterpret_cast<uint2*>(at) = uint2{flo, fhi};
     *reinterpret_cast<uint2*>(at + ind_off) = uint2{ilo, ihi};
-    return nfa | ilo | ihi;
+    return nfa;
 }
 
 // LDS: K tile, V^T tile, the tile's row scales, the waves' non-finite flags, then
@@ -533,7 +550,8 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
     };
     // registers -> LDS (K swizzled row-major, V transposed in contraction order);
     // with CHK, each wave records whether it staged a non-finite V value
-    auto store_tile = [&]() {
+    // split: the second staging of a tile that held an Inf or NaN (CHK only)
+    auto store_tile = [&](bool split) {
         uint32_t nfa = 0u;
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
@@ -580,7 +598,7 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                             hi2 = (vreg[i][2][w] & 0xffffu) | (vreg[i][3][w] << 16);
                         }
                     }
-                    if constexpr (CHK) nfa = store_v_checked<F16>(vt_lds + vt_off(ch * EPC + dd, gq) + 8 * kb, IND, lo2, hi2, nfa);
+                    if constexpr (CHK) nfa = store_v<F16>(vt_lds + vt_off(ch * EPC + dd, gq) + 8 * kb, IND, lo2, hi2, split, nfa);
                     else *reinterpret_cast<uint2*>(vt_lds + vt_off(ch * EPC + dd, gq) + 8 * kb) = uint2{lo2, hi2};
                 }
             }
@@ -592,8 +610,10 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
             }
         }
         if constexpr (CHK) {
-            const bool any = wave_any(nfa != 0u);
-            if (lane == 0) wflag[wave] = any ? 1u : 0u;
+            if (!split) {
+                const bool any = wave_any(nonfinite_found(nfa));
+                if (lane == 0) wflag[wave] = any ? 1u : 0u;
+            }
         }
     };
 
@@ -639,15 +659,20 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
         load_mask(0, mcur);
     }
     for (int t0 = 0; t0 < n_keys; t0 += kTK) {
-        store_tile();
+        store_tile(false);
         __syncthreads();
-        // a non-finite V value in this tile: P.V on the vector ALU with exact skips
+        // an Inf or NaN in this tile's V: staged again, split, before the registers
+        // take the next tile (uniform)
         bool flagged = false;
         if constexpr (CHK) {
             uint32_t f = 0u;
 #pragma unroll
             for (int w = 0; w < W; ++w) f |= wflag[w];
             flagged = f != 0u;
+            if (flagged) {
+                store_tile(true);
+                __syncthreads();
+            }
         }
         if (t0 + kTK < n_keys) {                          // in flight during this tile's math
             load_tile(t0 + kTK);
