@@ -78,12 +78,33 @@ def decode_traffic():
     return t["fetch_bytes"] + t["write_bytes"]
 
 
+def _tree_windows(np, gen):
+    wl = gen.config5(32000)
+    return dataclasses.replace(wl, tree_parent=np.tile(gen.heap_parents(16), (16, 1)).astype(np.int32),
+                               name="int8_tree_verify_decode_d32000")
+
+
+# decode workloads --only can time alone: name -> (np, gen) -> (workload, description)
+ONLY = {
+    "verify_decode_d12000": lambda np, gen: (gen.config5(12000), "int8 verify: 16 streams x 16-row causal windows, "
+                                             "48/4 heads, D=256, depth 12000, slices of 2048"),
+    "verify_decode_d32000": lambda np, gen: (gen.config5(32000), "int8 verify: 16 streams x 16-row causal windows, "
+                                             "48/4 heads, D=256, depth 32000, slices of 2048"),
+    "tree_verify_decode_d32000": lambda np, gen: (_tree_windows(np, gen), "int8 verify as at depth 32000, each "
+                                                  "window a 16-node binary tree in heap order"),
+    "fp8_decode": lambda np, gen: (gen.config2(kv_dtype="fp8"), "split-K decode as the headline with e4m3 K/V "
+                                   "rows + fp32 row scales"),
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=sorted(ONLY), default=None,
+                    help="time one decode workload alone (for profiling) and print its figures")
     return ap.parse_args()
 
 
@@ -331,6 +352,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     sa.lib()
+
+    if args.only:
+        wl, text = ONLY[args.only](np, gen)
+        out = time_decode(args.only, wl, args.steps, sa, hip_run, torch, np, text)
+        print(json.dumps({"workload": args.only, args.only: out}), flush=True)
+        return
 
     # ---- the headline workload (host generation, then resident in HBM) ----------
     log("generating the split-K decode workload")

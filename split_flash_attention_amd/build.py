@@ -10,7 +10,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libselattn.so")
-SOURCES = ["api.hip", "valu_attn.hip", "mfma_attn.hip", "mfma_decode.hip", "mfma_prefill.hip", "noalloc.hip"]
+SOURCES = ["api.hip", "valu_attn.hip", "mfma_attn.hip", "mfma_decode.hip", "mfma_prefill.hip", "noalloc.hip",
+           "wide_decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

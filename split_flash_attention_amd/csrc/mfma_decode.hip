@@ -1,10 +1,12 @@
 // Split-K decode and verify windows on the matrix-core kernels: one work-group
 // per (stream, kv head, slice[, query chunk]) (TensorFold PR #2595: the
 // attn_decode grid of rows, heads and slices), partials merged by the combine.
-// Up to 16 query vectors per unit run on the single-wave kernel, more on the
-// group kernel (one wave per 16 query vectors sharing each K/V tile).
+// Up to 16 query vectors per unit run on the single-wave kernel; int8 units of more
+// than 32 on the wide kernel (32-column blocks, one wave per SIMD); the others on
+// the group kernel (one wave per 16 query vectors sharing each K/V tile).
 #include "group_kernel.h"
 #include "lean_kernel.h"
+#include "wide_kernel.h"
 
 #include <algorithm>
 
@@ -36,6 +38,14 @@ hipError_t launch_mfma_decode(const sel_attn_decode_args& a, hipStream_t st) {
         p.qpw = 16;
         p.n_units_y = a.n_head_kv;
         return lean_launch<kDecode>(a.kv_dtype, p, dim3(n_sl, a.n_head_kv, a.n_stream), st);
+    }
+    const bool sc32 = static_cast<int64_t>(a.cap) * a.sc_stride_cell * 4 < (int64_t{1} << 31) - 64;
+    if (off32 && sc32 && wide_eligible(a.kv_dtype, a.head_dim, p.M)) {
+        // int8 verify windows: four waves of two 32-column blocks share each tile
+        p.qpw = kWQ;
+        const int nqc = (p.M + kWQ - 1) / kWQ;
+        p.n_units_y = a.n_head_kv * nqc;
+        return wide_launch(p, dim3(n_sl, a.n_head_kv * nqc, a.n_stream), st);
     }
     if (off32) {
         // many query vectors: one wave per block, a work-group shares each tile

@@ -1,5 +1,5 @@
-// One-wave probes on gfx950: the v_mfma_f32_16x16x32_{bf16,f16} lane layout, and
-// the e4m3 byte convert (below).
+// One-wave probes on gfx950: the v_mfma_f32_16x16x32_{bf16,f16} and
+// v_mfma_f32_32x32x16_bf16 lane layouts, and the e4m3 byte convert (below).
 // Each lane passes its own 8 A values and 8 B values (16-bit bit patterns) and
 // gets back its 4 accumulator values; the test checks them against the layout
 // the attention kernels assume.  Buffers: a, b [64][8] uint16; d [64][4] float.
@@ -23,6 +23,26 @@ __global__ void __launch_bounds__(64) probe(const uint16_t* a, const uint16_t* b
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                       __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
     for (int i = 0; i < 4; ++i) d[l * 4 + i] = acc[i];
+}
+
+// v_mfma_f32_32x32x16_bf16: 8 A and 8 B values per lane in, 16 accumulator values
+// per lane out (d [64][16] float).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__global__ void __launch_bounds__(64) probe32(const uint16_t* a, const uint16_t* b, float* d) {
+    const int l = threadIdx.x;
+    u16x8 av, bv;
+    for (int j = 0; j < 8; ++j) { av[j] = a[l * 8 + j]; bv[j] = b[l * 8 + j]; }
+    f32x16 acc;
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                  __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+    for (int i = 0; i < 16; ++i) d[l * 16 + i] = acc[i];
+}
+
+extern "C" int mfma32_probe(const void* a, const void* b, void* d, void* stream) {
+    hipLaunchKernelGGL(probe32, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), static_cast<float*>(d));
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 extern "C" int mfma_probe(const void* a, const void* b, void* d, int f16, void* stream) {
@@ -61,5 +81,31 @@ extern "C" int fp8_pk_probe(const void* w, void* out, void* stream) {
 extern "C" int fp8_probe(const void* w, void* out, void* stream) {
     hipLaunchKernelGGL(fp8_cvt, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
                        static_cast<const uint32_t*>(w), static_cast<float*>(out));
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Buffer range checking: a raw (stride 0) descriptor of num_records bytes over the
+// start of a larger, fully allocated buffer `src` (at least 4 * 256 bytes), read
+// with the same total offset carried either by the VGPR operand or by the SGPR
+// operand.  Lane l reads offset 4 l: out[l] through voffset, out[64 + l] through
+// soffset (voffset 0).  Every address lies inside `src`, whatever the check does.
+__global__ void __launch_bounds__(64) buffer_range(const uint32_t* src, uint32_t* out, int num_records) {
+    const int l = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(src), static_cast<short>(0), num_records, 0x00020000);
+    out[l] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * l, 0, 0);
+    // soffset must be uniform: lane l's value comes from a loop over the 64 offsets
+    uint32_t v = 0;
+    for (int i = 0; i < 64; ++i) {
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rs, 0, 4 * i, 0);
+        if (i == l) v = w;
+    }
+    out[64 + l] = v;
+}
+
+extern "C" int buffer_range_probe(const void* src, void* out, int num_records, void* stream) {
+    if (num_records < 0 || num_records > 256) return -1;
+    hipLaunchKernelGGL(buffer_range, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint32_t*>(src), static_cast<uint32_t*>(out), num_records);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -1,6 +1,6 @@
-"""The 16x16x32 MFMA lane layout and the e4m3 widening that the matrix-core
-kernels rely on, checked on the GPU with exact inputs (one wave, fixed 64-lane
-buffers)."""
+"""The 16x16x32 and 32x32x16 MFMA lane layouts and the e4m3 widening that the
+matrix-core kernels rely on, checked on the GPU with exact inputs (one wave,
+fixed 64-lane buffers)."""
 import ctypes
 import os
 
@@ -53,6 +53,42 @@ def test_mfma_16x16x32_layout(f16):
     assert np.array_equal(d.cpu().numpy(), expected(a_vals, b_vals))
 
 
+def expected32(a_vals, b_vals):
+    # A[m][k] held by lane (k // 8) * 32 + m, element k % 8; B[k][n] by lane (k // 8) * 32 + n;
+    # D[m][n] by lane (m // 4 % 2) * 32 + n, element (m // 8) * 4 + m % 4
+    A = np.zeros((32, 16))
+    B = np.zeros((16, 32))
+    for l in range(64):
+        for j in range(8):
+            A[l % 32, 8 * (l // 32) + j] = a_vals[l, j]
+            B[8 * (l // 32) + j, l % 32] = b_vals[l, j]
+    C = A @ B
+    d = np.zeros((64, 16))
+    for l in range(64):
+        for i in range(16):
+            d[l, i] = C[8 * (i // 4) + 4 * (l // 32) + i % 4, l % 32]
+    return d
+
+
+def test_mfma_32x32x16_bf16_layout():
+    if not torch.cuda.is_available():
+        pytest.fail("needs a GPU")
+    lib = ctypes.CDLL(LIB)
+    rng = np.random.default_rng(4)
+    a_vals = rng.integers(-4, 5, size=(64, 8)).astype(np.float32)
+    b_vals = rng.integers(-4, 5, size=(64, 8)).astype(np.float32)
+    a_bits = (a_vals.view(np.uint32) >> 16).astype(np.uint16)
+    b_bits = (b_vals.view(np.uint32) >> 16).astype(np.uint16)
+    a = torch.from_numpy(a_bits.view(np.int16).copy()).cuda()
+    b = torch.from_numpy(b_bits.view(np.int16).copy()).cuda()
+    d = torch.zeros((64, 16), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert lib.mfma32_probe(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                            ctypes.c_void_p(d.data_ptr()), ctypes.c_void_p(st)) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy(), expected32(a_vals, b_vals))
+
+
 def test_fp8_convert_matches_e4m3_definition():
     """v_cvt_f32_fp8 (the e4m3 widening the kernels use for fp8 K/V) on all 256
     codes equals the oracle's e4m3 values (TensorFold PR #911: e4m3, scale
@@ -99,3 +135,24 @@ def test_fp8_pair_convert_matches_e4m3_definition():
     assert np.array_equal(np.isnan(val), np.isnan(ref)), np.argwhere(np.isnan(val) != np.isnan(ref))[:8]
     fin = ~np.isnan(ref)
     assert np.array_equal(val[fin], ref[fin]), np.argwhere((val != ref) & fin)[:8]
+
+
+@pytest.mark.parametrize("num_records", [0, 64, 100, 256])
+def test_buffer_range_check_covers_scalar_offset(num_records):
+    """The kernels carry a tile's row offset in the scalar operand of their buffer
+    loads and rely on rows past the descriptor's end reading as zeros: reads past
+    num_records must return 0 whether the offset sits in the VGPR or the SGPR
+    operand (every address read lies inside the allocation)."""
+    if not torch.cuda.is_available():
+        pytest.fail("needs a GPU")
+    lib = ctypes.CDLL(LIB)
+    src = torch.arange(1, 1025, dtype=torch.int32, device="cuda")
+    out = torch.full((128,), -1, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert lib.buffer_range_probe(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                  num_records, ctypes.c_void_p(st)) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    want = np.where(np.arange(64) * 4 < num_records, np.arange(1, 65), 0)
+    assert np.array_equal(o[:64], want)
+    assert np.array_equal(o[64:], want)
