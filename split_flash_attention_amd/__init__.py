@@ -68,35 +68,41 @@ class SelAttnError(RuntimeError):
 _lib = None
 
 
+def load(path):
+    """Load a build of the library from `path` with the entry points typed as
+    below (lib() uses it for the in-tree build)."""
+    L = ctypes.CDLL(path)
+    for name, argt in (("sel_attn_decode", [ctypes.POINTER(DecodeArgs), _p]),
+                       ("sel_attn_split_combine", [ctypes.POINTER(CombineArgs), _p]),
+                       ("sel_attn_prefill", [ctypes.POINTER(PrefillArgs), _p]),
+                       ("sel_attn_supports", [ctypes.c_int, _p]),
+                       ("sel_attn_decode_workspace",
+                        [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t),
+                         ctypes.POINTER(ctypes.c_size_t)]),
+                       ("sel_attn_decode_path", [ctypes.POINTER(DecodeArgs)]),
+                       ("sel_attn_decode_noalloc", [ctypes.POINTER(DecodeArgs), _p, _p, _p]),
+                       ("sel_attn_prefill_path", [ctypes.POINTER(PrefillArgs)]),
+                       ("sel_attn_abi_version", []),
+                       ("sel_attn_args_size", [ctypes.c_int]),
+                       ("sel_attn_strerror", [ctypes.c_int])):
+        fn = getattr(L, name)
+        fn.argtypes = argt
+        fn.restype = ctypes.c_int
+    L.sel_attn_strerror.restype = ctypes.c_char_p
+    L.sel_attn_args_size.restype = ctypes.c_size_t
+    for op, cls in ((OP_DECODE, DecodeArgs), (OP_PREFILL, PrefillArgs), (OP_COMBINE, CombineArgs)):
+        if L.sel_attn_args_size(op) != ctypes.sizeof(cls):
+            raise ImportError(f"argument struct mismatch for op {op}")
+    return L
+
+
 def lib():
     """Load libselattn.so (built in-tree by build.build()); raise if absent."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is not built; run `python -m split_flash_attention_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        for name, argt in (("sel_attn_decode", [ctypes.POINTER(DecodeArgs), _p]),
-                           ("sel_attn_split_combine", [ctypes.POINTER(CombineArgs), _p]),
-                           ("sel_attn_prefill", [ctypes.POINTER(PrefillArgs), _p]),
-                           ("sel_attn_supports", [ctypes.c_int, _p]),
-                           ("sel_attn_decode_workspace",
-                            [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t),
-                             ctypes.POINTER(ctypes.c_size_t)]),
-                           ("sel_attn_decode_path", [ctypes.POINTER(DecodeArgs)]),
-                           ("sel_attn_decode_noalloc", [ctypes.POINTER(DecodeArgs), _p, _p, _p]),
-                           ("sel_attn_prefill_path", [ctypes.POINTER(PrefillArgs)]),
-                           ("sel_attn_abi_version", []),
-                           ("sel_attn_args_size", [ctypes.c_int]),
-                           ("sel_attn_strerror", [ctypes.c_int])):
-            fn = getattr(L, name)
-            fn.argtypes = argt
-            fn.restype = ctypes.c_int
-        L.sel_attn_strerror.restype = ctypes.c_char_p
-        L.sel_attn_args_size.restype = ctypes.c_size_t
-        for op, cls in ((OP_DECODE, DecodeArgs), (OP_PREFILL, PrefillArgs), (OP_COMBINE, CombineArgs)):
-            if L.sel_attn_args_size(op) != ctypes.sizeof(cls):
-                raise ImportError(f"argument struct mismatch for op {op}")
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
 
 

@@ -20,9 +20,23 @@ FLAGS = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(CSRC, "_build", src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Test-only builds with one planted mistake each: the GPU tests run named parity
+# tests through them and require each to fail.  name -> (translation unit, define).
+PLANTS = {
+    "combine_nan_to_zero": ("valu_attn.hip", "SELATTN_PLANT_COMBINE_NAN_TO_ZERO"),
+    "alibi_before_softcap": ("mfma_prefill.hip", "SELATTN_PLANT_ALIBI_BEFORE_SOFTCAP"),
+    "keep_repeats": ("mfma_prefill.hip", "SELATTN_PLANT_KEEP_REPEATS"),
+}
+PLANT_DIR = os.path.join(os.path.dirname(HERE), "tests", "planted")
+
+
+def plant_path(name):
+    return os.path.join(PLANT_DIR, f"libselattn_{name}.so")
+
+
+def _compile(src, define=None, tag=None):
+    obj = os.path.join(CSRC, "_build", src.replace(".hip", f".{tag}.o" if tag else ".o"))
+    cmd = [HIPCC, *FLAGS, *([f"-D{define}"] if define else []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in (r.stderr or "").splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)
@@ -53,16 +67,26 @@ def build_probe():
     return PROBE_OUT
 
 
-def build(verbose=False):
-    os.makedirs(os.path.join(CSRC, "_build"), exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose=False):
+    os.makedirs(os.path.join(CSRC, "_build"), exist_ok=True)
+    os.makedirs(PLANT_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        jobs = [ex.submit(_compile, src) for src in SOURCES]
+        pjobs = {name: ex.submit(_compile, src, define, name) for name, (src, define) in PLANTS.items()}
+        objs = [j.result() for j in jobs]
+        pobjs = {name: j.result() for name, j in pjobs.items()}
+    _link(objs, OUT)
+    for name, (src, _) in PLANTS.items():
+        _link([pobjs[name] if s == src else o for s, o in zip(SOURCES, objs)], plant_path(name))
     if os.path.exists(PROBE_SRC):
         build_probe()
     if verbose:

@@ -157,6 +157,22 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         int n_ids = 0;
         // an id is valid iff 0 <= id < nblk
         const int nblk = static_cast<int>((static_cast<int64_t>(p.n_kv) + p.bs - 1) / p.bs);
+#ifdef SELATTN_PLANT_KEEP_REPEATS
+        // test-only planted mistake (never in a product build): the valid ids in list
+        // order, repeats kept
+        if (nblk <= kLT * D * 2 * 8) {
+            for (int base = 0; base < p.n_sel; base += 64) {
+                const int e = base + lane;
+                const int x = e < p.n_sel ? srow[e] : -1;
+                const bool keep = x >= 0 && x < nblk;
+                const unsigned long long bal = __ballot(keep);
+                const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+                if (keep) list[n_ids + rank] = x;
+                n_ids += __popcll(bal);
+            }
+            __syncthreads();
+        } else
+#endif
         if (nblk <= kLT * D * 2 * 8) {
             // the row's valid ids as a bitmap over the blocks (in the K tile's LDS,
             // free until the first tile): set bits collapse repeats, and reading the

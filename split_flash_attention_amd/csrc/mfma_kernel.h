@@ -724,8 +724,14 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                 }
                 float x = s[k][kb][i];
                 if constexpr (B8) x *= ksc_lds[kb * 16 + 4 * lg + i];
+#ifdef SELATTN_PLANT_ALIBI_BEFORE_SOFTCAP
+                // test-only planted mistake (never in a product build): the bias first
+                x += slope[k] * static_cast<float>(cell - qv_pos[k]);
+                if (p.softcap > 0.f) x = p.softcap * tanhf(x / p.softcap);
+#else
                 if (p.softcap > 0.f) x = p.softcap * tanhf(x / p.softcap);
                 x += slope[k] * static_cast<float>(cell - qv_pos[k]);
+#endif
                 x += maskv;
                 vis[e] = v;
                 sc[e] = x;

@@ -440,7 +440,12 @@ __global__ __launch_bounds__(256) void combine_kernel(sel_attn_combine_args a, i
     const int sp = lane / L, c = lane - (lane / L) * L;
     if (nanf || M == kPosInf || M == kNegInf) {
         if (sp == 0) {
+#ifdef SELATTN_PLANT_COMBINE_NAN_TO_ZERO
+            // test-only planted mistake (never in a product build): NaN becomes 0
+            const float x = (!nanf && M == kPosInf) ? __builtin_nanf("") : 0.f;
+#else
             const float x = (nanf || M == kPosInf) ? __builtin_nanf("") : 0.f;
+#endif
             reinterpret_cast<float4*>(out)[c] = float4{x, x, x, x};
         }
         return;

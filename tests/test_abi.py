@@ -209,3 +209,18 @@ def test_noalloc_validates_before_any_device_call(L):
     a = good_decode(part_o=None, part_ml=None, n_head_q=30)                 # 30 % 4 != 0
     assert L.sel_attn_decode_noalloc(ctypes.byref(a), out, None, None) == sa.EINVAL
     assert sa.NOALLOC_SCRATCH_BYTES == 64 * 1024 * 1024
+
+
+def test_planted_variants_are_declared_and_guarded():
+    """Each planted-mistake build names a define that the sources guard with #ifdef
+    (so a product build, which sets none, never contains it) and a GPU control."""
+    import glob
+    from split_flash_attention_amd import build
+    from tests.test_gpu_planted import CONTROLS
+    assert set(build.PLANTS) == set(CONTROLS)
+    csrc = glob.glob(os.path.join(os.path.dirname(build.__file__), "csrc", "*"))
+    text = "".join(open(f).read() for f in csrc if f.endswith((".h", ".hip")))
+    for name, (src, define) in build.PLANTS.items():
+        assert src in build.SOURCES
+        assert f"#ifdef {define}" in text, define
+    assert "#define SELATTN_PLANT" not in text
