@@ -184,8 +184,9 @@ def decode_work(wl, np):
     return nbytes, flops
 
 
-def time_decode(name, wl, steps, sa, hip_run, torch, np, workload_text):
-    """Kernel-only and with-combine timings of one decode workload."""
+def time_decode(name, wl, steps, warmup, sa, hip_run, torch, np, workload_text):
+    """Kernel-only and with-combine timings of one decode workload, after `warmup`
+    untimed steps of it."""
     d = hip_run.DecodeDev(wl, "cuda", poison_outputs=False)
     a, c = d.args(), d.combine_args()
 
@@ -196,7 +197,8 @@ def time_decode(name, wl, steps, sa, hip_run, torch, np, workload_text):
         sa.sel_attn_decode(a)
         sa.sel_attn_split_combine(c)
 
-    step()
+    for _ in range(max(1, warmup)):
+        step()
     torch.cuda.synchronize()
     ms_k = timed(kernel, steps, torch)
     ms_s = timed(step, steps, torch)
@@ -355,7 +357,7 @@ def main():
 
     if args.only:
         wl, text = ONLY[args.only](np, gen)
-        out = time_decode(args.only, wl, args.steps, sa, hip_run, torch, np, text)
+        out = time_decode(args.only, wl, args.steps, args.warmup, sa, hip_run, torch, np, text)
         print(json.dumps({"workload": args.only, args.only: out}), flush=True)
         return
 
@@ -419,24 +421,24 @@ def main():
     log("generating and timing the int8 verify-window decode at depth 12000")
     wl5a = gen.config5(12000)
     result["verify_decode_d12000"] = time_decode(
-        "5a", wl5a, args.steps, sa, hip_run, torch, np,
+        "5a", wl5a, args.steps, args.warmup, sa, hip_run, torch, np,
         "int8 verify: 16 streams x 16-row causal windows, 48/4 heads, D=256, depth 12000, slices of 2048")
     del wl5a
     log("generating and timing the int8 verify-window decode at depth 32000 (chain and tree windows)")
     wl5 = gen.config5(32000)
     result["verify_decode_d32000"] = time_decode(
-        "5b", wl5, args.steps, sa, hip_run, torch, np,
+        "5b", wl5, args.steps, args.warmup, sa, hip_run, torch, np,
         "int8 verify: 16 streams x 16-row causal windows, 48/4 heads, D=256, depth 32000, slices of 2048")
     wl5t = dataclasses.replace(wl5, tree_parent=np.tile(gen.heap_parents(16), (16, 1)).astype(np.int32),
                                name="int8_tree_verify_decode_d32000")
     result["tree_verify_decode_d32000"] = time_decode(
-        "5t", wl5t, args.steps, sa, hip_run, torch, np,
+        "5t", wl5t, args.steps, args.warmup, sa, hip_run, torch, np,
         "int8 verify as at depth 32000, each window a 16-node binary tree in heap order")
     del wl5t
     log("generating and timing the split-K decode with e4m3 K/V")
     wl2f = gen.config2(kv_dtype="fp8")
     result["fp8_decode"] = time_decode(
-        "2f", wl2f, args.steps, sa, hip_run, torch, np,
+        "2f", wl2f, args.steps, args.warmup, sa, hip_run, torch, np,
         "split-K decode as the headline with e4m3 K/V rows + fp32 row scales")
     del wl2f
 

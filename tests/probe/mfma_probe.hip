@@ -109,3 +109,30 @@ extern "C" int buffer_range_probe(const void* src, void* out, int num_records, v
                        static_cast<const uint32_t*>(src), static_cast<uint32_t*>(out), num_records);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
+
+// Buffer loads straight into LDS (buffer_load_dwordx4 ... lds): wave w's lanes
+// read 16 bytes each from src at offset 16 * perm(l), perm(l) = 63 - l, and the
+// load deposits them in LDS at base + 1 KiB w; the LDS contents are then copied
+// out as they lie.  src >= 4 KiB, out [256][4] uint32 (4 waves).
+__global__ void __launch_bounds__(256) lds_dma(const uint32_t* src, uint32_t* out) {
+    extern __shared__ __align__(16) char lds[];
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(src), static_cast<short>(0), 4096, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(lds + 1024 * w), 16,
+        1024 * w + 16 * (63 - l), 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const uint4 v = reinterpret_cast<const uint4*>(lds)[threadIdx.x];
+    out[threadIdx.x * 4 + 0] = v.x;
+    out[threadIdx.x * 4 + 1] = v.y;
+    out[threadIdx.x * 4 + 2] = v.z;
+    out[threadIdx.x * 4 + 3] = v.w;
+}
+
+extern "C" int lds_dma_probe(const void* src, void* out, void* stream) {
+    hipLaunchKernelGGL(lds_dma, dim3(1), dim3(256), 4096, static_cast<hipStream_t>(stream),
+                       static_cast<const uint32_t*>(src), static_cast<uint32_t*>(out));
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}

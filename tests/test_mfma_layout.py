@@ -156,3 +156,21 @@ def test_buffer_range_check_covers_scalar_offset(num_records):
     want = np.where(np.arange(64) * 4 < num_records, np.arange(1, 65), 0)
     assert np.array_equal(o[:64], want)
     assert np.array_equal(o[64:], want)
+
+
+def test_buffer_load_to_lds_places_lane_l_at_16l():
+    """buffer_load_dwordx4 ... lds (the wide int8 kernel stages raw tiles this way):
+    lane l's 16 bytes land at the wave's LDS base + 16 l, whatever address it read."""
+    if not torch.cuda.is_available():
+        pytest.fail("needs a GPU")
+    lib = ctypes.CDLL(LIB)
+    src = torch.arange(1024, dtype=torch.int32, device="cuda")
+    out = torch.full((256, 4), -1, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert lib.lds_dma_probe(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                             ctypes.c_void_p(st)) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    s = np.arange(1024).reshape(4, 64, 4)           # [wave][16-byte chunk][word]
+    want = s[:, ::-1, :].reshape(256, 4)            # lane l of wave w read chunk 63 - l
+    assert np.array_equal(o, want)
