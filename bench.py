@@ -103,13 +103,29 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=sorted(ONLY), default=None,
-                    help="time one decode workload alone (for profiling) and print its figures")
+    ap.add_argument("--only", choices=sorted(ONLY) + ["sel_prefill"], default=None,
+                    help="time one workload alone (for profiling) and print its figures")
     return ap.parse_args()
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def settle(fn, warmup, torch, min_s=0.3):
+    """Untimed calls of `fn` before a measurement: at least `warmup` of them and at
+    least `min_s` seconds of them, so that the clocks have left their idle state
+    after the host-side generation of the workload."""
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 1
+    while n < warmup or time.perf_counter() - t0 < min_s:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 def timed(fn, steps, torch):
@@ -197,9 +213,7 @@ def time_decode(name, wl, steps, warmup, sa, hip_run, torch, np, workload_text):
         sa.sel_attn_decode(a)
         sa.sel_attn_split_combine(c)
 
-    for _ in range(max(1, warmup)):
-        step()
-    torch.cuda.synchronize()
+    settle(step, warmup, torch)
     ms_k = timed(kernel, steps, torch)
     ms_s = timed(step, steps, torch)
     k_med, k_min = timed_each(kernel, steps, torch)
@@ -249,7 +263,7 @@ def gather_roof(wl, k, v, torch, np):
     groups = 1024
     out = torch.empty(groups * 4, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
-    best = 0.0
+    per_unroll = {}
     for unroll in (4, 8, 16):
         def run():
             rc = lib.gather_probe(kv.data_ptr(), idx.data_ptr(), ustart.data_ptr(), n_units, hkv,
@@ -258,8 +272,8 @@ def gather_roof(wl, k, v, torch, np):
             assert rc == 0, rc
         run()
         ms = timed_each(run, 10, torch)[1]
-        best = max(best, idx.numel() * wl.block_size * row_bytes / (ms * 1e-3) / 1e9)
-    return best
+        per_unroll[unroll] = idx.numel() * wl.block_size * row_bytes / (ms * 1e-3) / 1e9
+    return max(per_unroll.values()), per_unroll
 
 
 def sel_cells(wl, np):
@@ -339,6 +353,67 @@ def cpu_baseline(wl2, wl3, wl5, np, budget_s=8.0):
     return res
 
 
+def time_sel_prefill(wl3, steps, warmup, sa, hip_run, torch, np):
+    """The selected-key prefill workload: kernel timings (warm, one by one, and after a
+    write that evicts the Infinity Cache) and its gather roof."""
+    d3 = hip_run.PrefillDev(wl3, "cuda", poison_outputs=False)
+    a3 = d3.args()
+
+    def prefill():
+        sa.sel_attn_prefill(a3)
+
+    settle(prefill, warmup, torch)
+    ms_prefill = timed(prefill, steps, torch)
+    pre_med, pre_min = timed_each(prefill, steps, torch)
+    flush_buf = torch.empty(1 << 27, dtype=torch.float32, device="cuda")       # 512 MiB
+    ms_prefill_cold = timed_cold(prefill, lambda: flush_buf.fill_(0.5), 5, torch)
+    del flush_buf
+    gather_gbs, per_unroll = gather_roof(wl3, d3.k, d3.v, torch, np)
+    n_cells = sel_cells(wl3, np)
+    flops3 = 4.0 * wl3.head_dim * wl3.n_head_q * n_cells
+    gather3 = n_cells * wl3.n_head_kv * wl3.head_dim * 2 * 2
+    tflops3 = flops3 / (ms_prefill * 1e-3) / 1e12
+    return {"workload": "2048 rows x 512 block ids (4-cell blocks), 16/2 heads, D=256, bf16",
+            "ms": round(ms_prefill, 5), "ms_median": round(pre_med, 5),
+            "ms_min": round(pre_min, 5), "ms_cold": round(ms_prefill_cold, 5),
+            "gflop": round(flops3 / 1e9, 3),
+            "tflops": round(tflops3, 3),
+            "mfma_peak_frac": round(tflops3 / BF16_PEAK_TFLOPS, 5),
+            "gathered_gbs": round(gather3 / (ms_prefill * 1e-3) / 1e9, 2),
+            "gather_roof_gbs": round(gather_gbs, 1),
+            "gather_roof_frac": round(gather3 / (ms_prefill * 1e-3) / 1e9 / gather_gbs, 4),
+            "gather_probe_gbs_by_blocks_in_flight": {str(k): round(v, 1) for k, v in per_unroll.items()},
+            "tokens_per_s": round(wl3.n_row / (ms_prefill * 1e-3), 1),
+            "prefill_path": sa.prefill_path(a3)}
+
+
+def memory_roofs(torch):
+    """Read bandwidth (GB/s) of each level of the memory hierarchy, from the window
+    probe: random 1 KiB chunks of a resident window of 16 KiB (L1), 2 MiB (L2 of each
+    accelerator die), 64 MiB (Infinity Cache) and 2 GiB (HBM)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "tests", "probe", "libgather_probe.so"))
+    lib.window_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    groups, iters = 2048, 1024
+    out = torch.empty(groups * 4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for name, kib in (("l1_16KiB", 16), ("l2_2MiB", 2048), ("infinity_cache_64MiB", 65536),
+                      ("hbm_2GiB", 2 << 20)):
+        buf = torch.ones(kib * 256, dtype=torch.float32, device="cuda")
+
+        def run():
+            rc = lib.window_read_probe(buf.data_ptr(), kib, iters, out.data_ptr(), groups, stream)
+            assert rc == 0, rc
+        for _ in range(3):
+            run()
+        ms = timed_each(run, 10, torch)[0]
+        res[name] = round(groups * 4 * iters * 1024 / (ms * 1e-3) / 1e9, 1)
+        del buf
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -355,6 +430,11 @@ def main():
     torch.cuda.set_device(0)
     sa.lib()
 
+    if args.only == "sel_prefill":
+        out = time_sel_prefill(gen.config3(), args.steps, args.warmup, sa, hip_run, torch, np)
+        out["memory_read_gbs"] = memory_roofs(torch)
+        print(json.dumps({"workload": args.only, args.only: out}), flush=True)
+        return
     if args.only:
         wl, text = ONLY[args.only](np, gen)
         out = time_decode(args.only, wl, args.steps, args.warmup, sa, hip_run, torch, np, text)
@@ -443,17 +523,14 @@ def main():
     del wl2f
 
     # ---- selected-key prefill and decode ------------------------------------------
-    log("generating the selected-key workloads")
+    log("selected-key prefill")
     wl3 = gen.config3()
-    d3 = hip_run.PrefillDev(wl3, "cuda", poison_outputs=False)
-    a3 = d3.args()
+    result["sel_prefill"] = time_sel_prefill(wl3, args.steps, args.warmup, sa, hip_run, torch, np)
+    log("selected-key decode")
     wl6 = gen.sel_decode()
     d6 = hip_run.PrefillDev(wl6, "cuda", n_splits=SEL_DECODE_SPLITS, poison_outputs=False)
     a6 = d6.args()
     c6 = sa.combine_args(part_o=d6.part_o, part_ml=d6.part_ml, out=d6.out.view(1, *d6.out.shape))
-
-    def prefill():
-        sa.sel_attn_prefill(a3)
 
     def sel_decode():
         sa.sel_attn_prefill(a6)
@@ -462,34 +539,10 @@ def main():
     def sel_decode_kernel():
         sa.sel_attn_prefill(a6)
 
-    log("timing the selected-key workloads")
-    for _ in range(args.warmup):
-        prefill()
-        sel_decode()
-    ms_prefill = timed(prefill, args.steps, torch)
-    pre_med, pre_min = timed_each(prefill, args.steps, torch)
+    settle(sel_decode, args.warmup, torch)
     ms_sd = timed(sel_decode, args.steps, torch)
     ms_sdk = timed(sel_decode_kernel, args.steps, torch)
     sd_med, sd_min = timed_each(sel_decode, args.steps, torch)
-    flush_buf = torch.empty(1 << 27, dtype=torch.float32, device="cuda")       # 512 MiB
-    ms_prefill_cold = timed_cold(prefill, lambda: flush_buf.fill_(0.5), 5, torch)
-    del flush_buf
-    gather_gbs = gather_roof(wl3, d3.k, d3.v, torch, np)
-    n_cells = sel_cells(wl3, np)
-    flops3 = 4.0 * wl3.head_dim * wl3.n_head_q * n_cells
-    gather3 = n_cells * wl3.n_head_kv * wl3.head_dim * 2 * 2
-    tflops3 = flops3 / (ms_prefill * 1e-3) / 1e12
-    result["sel_prefill"] = {"workload": "2048 rows x 512 block ids (4-cell blocks), 16/2 heads, D=256, bf16",
-                             "ms": round(ms_prefill, 5), "ms_median": round(pre_med, 5),
-                             "ms_min": round(pre_min, 5), "ms_cold": round(ms_prefill_cold, 5),
-                             "gflop": round(flops3 / 1e9, 3),
-                             "tflops": round(tflops3, 3),
-                             "mfma_peak_frac": round(tflops3 / BF16_PEAK_TFLOPS, 5),
-                             "gathered_gbs": round(gather3 / (ms_prefill * 1e-3) / 1e9, 2),
-                             "gather_roof_gbs": round(gather_gbs, 1),
-                             "gather_roof_frac": round(gather3 / (ms_prefill * 1e-3) / 1e9 / gather_gbs, 4),
-                             "tokens_per_s": round(wl3.n_row / (ms_prefill * 1e-3), 1),
-                             "prefill_path": sa.prefill_path(a3)}
     cells6 = sel_cells(wl6, np)
     flops6 = 4.0 * wl6.head_dim * wl6.n_head_q * cells6
     gather6 = cells6 * wl6.n_head_kv * wl6.head_dim * 2 * 2
@@ -543,7 +596,7 @@ def main():
     result["roofs"] = {"hbm_peak_gbs": HBM_PEAK_GBS, "bf16_mfma_peak_tflops": BF16_PEAK_TFLOPS,
                        "copy_gbs": round(copy_gbs, 1),
                        "bf16_matmul_tflops": round(2.0 * 8192 ** 3 / (ms_mm * 1e-3) / 1e12, 1),
-                       "sel_gather_gbs": round(gather_gbs, 1)}
+                       "sel_gather_gbs": result["sel_prefill"]["gather_roof_gbs"]}
     result["copy_gbs"] = round(copy_gbs, 1)
 
     if not args.no_cpu_baseline:

@@ -27,6 +27,19 @@ constexpr int kLT = 16;          // keys per tile
 __device__ __forceinline__ int k16_off(int key, int ch, int D) {
     return key * D * 2 + ((ch ^ (key & 15)) << 4);
 }
+// V staging task e: keys 4 kg .. 4 kg + 3 of the tile, 16-byte chunk ch of their rows.
+// Lanes 4q .. 4q + 3 take the same keys and consecutive chunks, so each lane quad of a
+// load reads 64 contiguous bytes of one row (one cache tag lookup instead of four);
+// each half-wave still covers four key groups of eight chunks, the set the V^T
+// writes below are free of bank conflicts for.
+template <int GCH>
+__device__ __forceinline__ void v_task(int e, int& kg, int& ch) {
+    constexpr int C = GCH < 8 ? GCH : 8;
+    const int r = e % (4 * C);
+    kg = r / C;
+    ch = (e / (4 * C)) * C + r % C;
+}
+
 // V^T tile: row d holds 16 keys (32 bytes, four 8-byte slots of 4 keys).  Row d is
 // stored at pr = d ^ ((d >> 3) & 7) and slot s at s ^ (2 * ((pr >> 3) & 1)): both the
 // 16-row operand reads and the 32-lane staging writes then hit distinct banks.
@@ -58,7 +71,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     constexpr int NDB = D / 16;
     constexpr int GCH = B8 ? D / 16 : D / 8;        // 16-byte chunks per K/V row in memory
     constexpr int K_TASKS = kLT * GCH;              // one 16-byte load each
-    constexpr int V_TASKS = 4 * GCH;                // task e: keys 4*(e & 3) + 0..3, chunk e >> 2
+    constexpr int V_TASKS = 4 * GCH;                // task e: keys 4 kg + 0..3, chunk ch (v_task)
     constexpr int NKL = (K_TASKS + 63) / 64;
     constexpr int NVL = (V_TASKS + 63) / 64;
     constexpr int EPC = B8 ? 16 : 8;
@@ -325,7 +338,9 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     // lines); the default when several query chunks share it through the L2.
     constexpr int kStream = CP;
     const int voff_k = (lane / GCH) * cb + (lane % GCH) * 16;            // decode: K task of lane
-    const int voff_v = 4 * (lane & 3) * cb + (lane >> 2) * 16;           // decode: V task of lane
+    int vkg0, vch0;                                                       // V task of lane (the
+    v_task<GCH>(lane, vkg0, vch0);                                        // i-th load adds 16 i chunks)
+    const int voff_v = 4 * vkg0 * cb + vch0 * 16;                         // decode: V task of lane
 
     u32x4 kreg[NKL];
     u32x4 vreg[NVL][4];
@@ -351,8 +366,10 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if constexpr (MODE == kSel) {
-                    const int cell = e < V_TASKS ? tc[4 * (e & 3) + j] : -1;
-                    const int off = cell >= 0 ? cell * cb + (e >> 2) * 16 : kAbsent;
+                    int kg, ch;
+                    v_task<GCH>(e, kg, ch);
+                    const int cell = e < V_TASKS ? tc[4 * kg + j] : -1;
+                    const int off = cell >= 0 ? cell * cb + ch * 16 : kAbsent;
                     vreg[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
                 } else {
                     const int off = e < V_TASKS ? voff_v : kAbsent;
@@ -403,7 +420,8 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         for (int i = 0; i < NVL; ++i) {
             const int e = lane + 64 * i;
             if (e < V_TASKS) {
-                const int kg = e & 3, ch = e >> 2;
+                int kg, ch;
+                v_task<GCH>(e, kg, ch);
                 if constexpr (B8) {
                     // dims dd, dd + 1 (bytes of half (dd >> 1) & 1 of word dd >> 2) at once
 #pragma unroll

@@ -57,7 +57,46 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* base, const int
     out[wave] = acc;
 }
 
+// Read bandwidth of one level of the memory hierarchy: every wave reads `iters`
+// 1 KiB chunks (16 bytes a lane, one load per chunk) of a window of n_chunks KiB,
+// each chunk drawn by a per-wave linear congruential sequence, U loads in flight.
+// A window that fits a cache level (but not the one above it) measures that level.
+template <int U>
+__global__ __launch_bounds__(256) void window_read_kernel(const char* base, unsigned chunk_mask, int iters,
+                                                          uint32_t* out) {
+    const int lane = threadIdx.x & 63;
+    const int wave = (blockIdx.x * 256 + threadIdx.x) >> 6;
+    uint32_t x = static_cast<uint32_t>(wave) * 2654435761u + 12345u;   // the same in every lane
+    uint32_t acc = 0;
+    for (int it = 0; it < iters; it += U) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            x = x * 1664525u + 1013904223u;
+            const unsigned c = (x >> 8) & chunk_mask;
+            v[u] = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(c) * 1024 + lane * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    out[wave] = acc;
+}
+
 }  // namespace
+
+// Host entry of the window probe: `base` holds n_chunks KiB (a power of two);
+// `groups` work-groups of 256 threads, each wave reading `iters` chunks (a multiple
+// of 8); `out` holds one word per wave.  Returns 0, -1 for arguments the kernel
+// does not take, -2 on a launch error.
+extern "C" int window_read_probe(const void* base, int n_chunks, int iters, uint32_t* out, int groups,
+                                 void* stream) {
+    if (!base || !out || n_chunks < 1 || (n_chunks & (n_chunks - 1)) != 0 || iters < 8 || iters % 8 != 0 ||
+        groups < 1)
+        return -1;
+    hipLaunchKernelGGL(window_read_kernel<8>, dim3(groups), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const char*>(base), static_cast<unsigned>(n_chunks - 1), iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
 
 // Host entry: unit u covers idx[unit_start[u] .. unit_start[u + 1]); launches
 // `groups` work-groups of 256 threads; `out` holds one word per wave (4 * groups
