@@ -55,6 +55,18 @@ template <int D>
 constexpr int lean_base_smem() {
     return kLT * D * 2 + D * 32 + 2 * kLT * 4 + 2 * kLT * 4 + 16 * 3 * 8 + 16 * 8;
 }
+// Decode with int8 / e4m3 rows streams its raw tiles straight into LDS, two tiles
+// ahead, through buffer loads that carry the LDS destination: a raw tile is K
+// [kLT][D] bytes, V [kLT][D] bytes, then 64 K and 64 V row scales (loaded for 64
+// keys, the first kLT used).  Two raw tiles take the place of the 16-bit K tile,
+// which these rows do not use: their score products read K's raw bytes.
+template <int D>
+constexpr int lean_raw_tile() { return 2 * kLT * D + 2 * 64 * 4; }
+template <int D>
+constexpr int lean_raw_extra() { return 2 * lean_raw_tile<D>() - kLT * D * 2; }
+template <int MODE, int KT>
+constexpr bool lean_raw(int) { return MODE == kDecode && byte_kv(KT); }
+
 // The tiles of a unit may be seen in part by some of its query vectors (decode with
 // MIX), and their V may hold Inf or NaN (not int8).
 template <int MODE, int KT, bool MIX>
@@ -83,8 +95,11 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     constexpr bool CHK = lean_check<MODE, KT, MIX>(0);
     constexpr int IND = lean_base_smem<D>() - kLT * D * 2;
 
-    char* k_lds = smem;
-    char* vt_lds = smem + kLT * D * 2;
+    // RAW: raw tiles in LDS (decode with byte rows); otherwise register-staged tiles
+    constexpr bool RAW = lean_raw<MODE, KT>(0);
+    constexpr int RAWB = lean_raw_tile<D>();
+    char* k_lds = smem;                          // 16-bit K tile, or (RAW) the two raw tiles
+    char* vt_lds = smem + (RAW ? 2 * RAWB : kLT * D * 2);
     float* ksc_lds = reinterpret_cast<float*>(vt_lds + D * 32);
     float* vsc_lds = ksc_lds + kLT;
     int* tcell = reinterpret_cast<int*>(vsc_lds + kLT);                       // [2][kLT]
@@ -342,6 +357,41 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     v_task<GCH>(lane, vkg0, vch0);                                        // i-th load adds 16 i chunks)
     const int voff_v = 4 * vkg0 * cb + vch0 * 16;                         // decode: V task of lane
 
+    // RAW: raw tile `buf` of the tile starting at key t0.  Load c of K (and of V)
+    // fills its bytes 1024 c .. 1024 c + 1023, lane l the 16 at 1024 c + 16 l: key
+    // (1024 c + 16 l) / D, slot s = ((1024 c + 16 l) mod D) / 16 of the row, which
+    // holds 16-byte chunk s ^ ksw(key) of K (s ^ vsw(key) of V) so that the operand
+    // and staging reads below meet no bank conflicts.  Lane l of the two scale loads
+    // takes key l.  2 NRK + 2 loads a tile, all of the wave.
+    constexpr int NRK = kLT * D / 1024;
+    constexpr int NDT = 2 * NRK + 2;
+    auto ksw = [](int key) { return key & (GCH - 1); };
+    auto vsw = [](int key) { return GCH >= 16 ? 8 * ((key >> 2) & 1) : 0; };
+    auto dma_tile = [&](int t0, int buf) __attribute__((always_inline)) {
+        if constexpr (RAW) {
+            const int scb = static_cast<int>(p.sc_sc) * 4;
+            const int nsc = n_keys > 0 ? (n_keys - 1) * scb + 4 : 0;
+            const int64_t sc_first = sc_base + static_cast<int64_t>(lo) * p.sc_sc;
+            const i32x4_t krw = raw_rsrc(kbase, nrec), vrw = raw_rsrc(vbase, nrec);
+            const i32x4_t ksr = raw_rsrc(p.ksc + sc_first, nsc), vsr = raw_rsrc(p.vsc + sc_first, nsc);
+            char* raw = smem + buf * RAWB;
+            int l = lane;
+            asm volatile("" : "+v"(l));            // recomputed here, not held across the loop
+            // the tile's previous contents have been read (the last K operand read
+            // fed a matrix instruction already issued; staging ran earlier)
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int c = 0; c < NRK; ++c) {
+                const int pos = 1024 * c + 16 * l;
+                const int key = pos / D, slot = (pos % D) >> 4;
+                lds_dma<16>(krw, lds_addr(raw + 1024 * c), key * cb + ((slot ^ ksw(key)) << 4), t0 * cb);
+                lds_dma<16>(vrw, lds_addr(raw + kLT * D + 1024 * c), key * cb + ((slot ^ vsw(key)) << 4), t0 * cb);
+            }
+            lds_dma<4>(ksr, lds_addr(raw + 2 * kLT * D), l * scb, t0 * scb);
+            lds_dma<4>(vsr, lds_addr(raw + 2 * kLT * D + 256), l * scb, t0 * scb);
+        }
+    };
+
     u32x4 kreg[NKL];
     u32x4 vreg[NVL][4];
     float kscr = 0.f, vscr = 0.f;
@@ -392,12 +442,14 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     // query vector sees in part); 2: V split into its finite part and indicator (the
     // second staging of a checked tile that held one).  Returns (wave-uniform) whether
     // a checked tile held one.
-    auto store_tile = [&](int mode) -> bool {
+    // (RAW: from raw tile `buf` in LDS; K stays raw, its operands are widened as read)
+    auto store_tile = [&](int mode, int buf) -> bool {
         uint32_t nfa = 0u;
+        const char* raw = smem + buf * RAWB;
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
             const int e = lane + 64 * i;
-            if (e < K_TASKS) {
+            if (!RAW && e < K_TASKS) {
                 const int key = e / GCH, ch = e % GCH;
                 if constexpr (B8) {
                     const u32x4 rw = kreg[i];
@@ -423,13 +475,23 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                 int kg, ch;
                 v_task<GCH>(e, kg, ch);
                 if constexpr (B8) {
+                    u32x4 vw[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if constexpr (RAW) {
+                            const int key = 4 * kg + j;
+                            vw[j] = *reinterpret_cast<const u32x4*>(raw + kLT * D + key * D + ((ch ^ vsw(key)) << 4));
+                        } else {
+                            vw[j] = vreg[i][j];
+                        }
+                    }
                     // dims dd, dd + 1 (bytes of half (dd >> 1) & 1 of word dd >> 2) at once
 #pragma unroll
                     for (int dd = 0; dd < EPC; dd += 2) {
                         const int w = dd >> 2, h = (dd >> 1) & 1;
                         uint32_t lo_e, lo_o, hi_e, hi_o;
-                        vpairs_bf16<KT>(vreg[i][0][w], vreg[i][1][w], h, lo_e, lo_o);
-                        vpairs_bf16<KT>(vreg[i][2][w], vreg[i][3][w], h, hi_e, hi_o);
+                        vpairs_bf16<KT>(vw[0][w], vw[1][w], h, lo_e, lo_o);
+                        vpairs_bf16<KT>(vw[2][w], vw[3][w], h, hi_e, hi_o);
                         if (CHK && mode != 0) {
                             nfa = store_v<F16>(vt_lds + vt16_off(ch * EPC + dd, kg), IND, lo_e, hi_e, mode == 2, nfa);
                             nfa = store_v<F16>(vt_lds + vt16_off(ch * EPC + dd + 1, kg), IND, lo_o, hi_o, mode == 2, nfa);
@@ -458,8 +520,13 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         }
         if constexpr (B8) {
             if (lane < kLT) {
-                ksc_lds[lane] = kscr;
-                vsc_lds[lane] = vscr;
+                if constexpr (RAW) {
+                    ksc_lds[lane] = reinterpret_cast<const float*>(raw + 2 * kLT * D)[lane];
+                    vsc_lds[lane] = reinterpret_cast<const float*>(raw + 2 * kLT * D + 256)[lane];
+                } else {
+                    ksc_lds[lane] = kscr;
+                    vsc_lds[lane] = vscr;
+                }
             }
         }
         if constexpr (CHK) return mode == 1 && wave_any(nonfinite_found(nfa));
@@ -488,26 +555,57 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         kread[q] = ln * D * 2 + (((q * 4 + lg) ^ ln) << 4);
         vread[q] = (ln ^ ((2 * q + (ln >> 3)) & 7)) * 32 + ((lg ^ (((ln >> 3) & 1) << 1)) << 3);
     }
+    // RAW: the 8 bytes of dims 8 (4 kk + lg) .. + 7 of key ln lie in chunk c = 2 kk +
+    // (lg >> 1), half lg & 1, stored at slot c ^ ksw(ln): the byte offset is
+    // kraw ^ (kk << 5) (the slot bits above bit 0 hold kk ^ (ln >> 1))
+    const int kraw = ln * D + ((((lg >> 1) ^ (ln & 1)) << 4) | ((lg & 1) << 3)) +
+                     ((((ln >> 1) & (GCH / 2 - 1))) << 5);
 
     if (n_keys > 0) {
         fill_cells(0);
         __syncthreads();                        // tcell written by lanes 0..15, read by all
-        load_tile(0);
+        if constexpr (RAW) {
+            dma_tile(0, 0);
+            if (kLT < n_keys) dma_tile(kLT, 1);
+        } else {
+            load_tile(0);
+        }
     }
     for (int t0 = 0; t0 < n_keys; t0 += kLT) {
+        const int buf = (t0 / kLT) & 1;
+        if constexpr (RAW) {
+            // raw tile t0 has landed (the next one's loads may still be in flight)
+            if (t0 + kLT < n_keys) wait_vm<NDT>();
+            else wait_vm<0>();
+        }
         // uniform: every query vector sees the whole tile
         const bool full = (MODE == kDecode) && t0 + kLT <= n_full;
-        const bool flagged = store_tile(CHK && !full ? 1 : 0);
-        if (flagged) store_tile(2);                    // the registers still hold the tile
+        const bool flagged = store_tile(CHK && !full ? 1 : 0, buf);
+        if (flagged) store_tile(2, buf);               // the registers (raw tile) still hold the tile
         if (t0 + kLT < n_keys) fill_cells(t0 + kLT);
         __syncthreads();
-        if (t0 + kLT < n_keys) load_tile(t0 + kLT);
+        if constexpr (!RAW) {
+            if (t0 + kLT < n_keys) load_tile(t0 + kLT);
+        }
 
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (RAW) {
+            const char* kr = smem + buf * RAWB;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(k_lds + kread[kk & 3] + (kk >> 2) * 256);
-            s = mfma16x16x32<F16>(a, qop[kk], s);
+            for (int kk = 0; kk < NKK; ++kk) {
+                const uint2 w = *reinterpret_cast<const uint2*>(kr + (kraw ^ (kk << 5)));
+                const u32x4 a = u32x4{kpair_bf16<KT>(w.x, 0), kpair_bf16<KT>(w.x, 1), kpair_bf16<KT>(w.y, 0),
+                                      kpair_bf16<KT>(w.y, 1)};
+                s = mfma16x16x32<F16>(a, qop[kk], s);
+            }
+            // the raw tile two ahead goes into this buffer, whose K, V and scales are read
+            if (t0 + 2 * kLT < n_keys) dma_tile(t0 + 2 * kLT, buf);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(k_lds + kread[kk & 3] + (kk >> 2) * 256);
+                s = mfma16x16x32<F16>(a, qop[kk], s);
+            }
         }
 
         // scores of keys 4 * lg + i of the tile: scale (int8 key scale), softcap,
@@ -706,7 +804,7 @@ int lean_resident_groups(int smem) {
 template <int MODE, int KT, int D, int CP, bool TREE, bool MIX>
 hipError_t lean_launch_one(const MParams& p, dim3 grid, hipStream_t st) {
     const int smem = lean_base_smem<D>() + (MODE == kSel ? p.sel_pow2 * 4 : 0) +
-                     (lean_check<MODE, KT, MIX>(0) ? D * 32 : 0);
+                     (lean_check<MODE, KT, MIX>(0) ? D * 32 : 0) + (lean_raw<MODE, KT>(0) ? lean_raw_extra<D>() : 0);
     if constexpr (MODE == kDecode) {
         const long long items = static_cast<long long>(grid.x) * grid.y * grid.z;
         grid = dim3(decode_grid(items, lean_resident_groups<MODE, KT, D, CP, TREE, MIX>(smem)), 1, 1);

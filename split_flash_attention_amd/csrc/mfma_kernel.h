@@ -152,6 +152,50 @@ __device__ __forceinline__ float byte_float(uint32_t word, int byte) {
     }
 }
 
+// wait until at most N of the wave's buffer loads are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
+
+// Buffer load of 4 or 16 bytes a lane straight into LDS at lds + 4 or 16 lane (M0
+// holds lds, one wait state after it is written; restored afterwards).  Written as
+// asm so that the compiler, which cannot tell which LDS bytes such a load writes,
+// does not put a wait for it in front of every later LDS read, nor count it among
+// the loads it waits for; a loop waits for its raw tiles itself (wait_vm) before
+// anything reads them.  No VGPR is written.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t raw_rsrc(const void* base, int num_records) {
+    const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+    i32x4_t r;
+    r[0] = static_cast<int>(a & 0xffffffffull);
+    r[1] = static_cast<int>((a >> 32) & 0xffffull);      // stride 0
+    r[2] = num_records;
+    r[3] = 0x00020000;
+    return r;
+}
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const i32x4_t& rs, unsigned lds, int voff, int soff) {
+    static_assert(BYTES == 4 || BYTES == 16, "dword or dwordx4");
+    int m0_saved;
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(m0_saved)
+                     : "s"(lds), "v"(voff), "s"(rs), "s"(soff)
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, %4 offen lds\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(m0_saved)
+                     : "s"(lds), "v"(voff), "s"(rs), "s"(soff)
+                     : "memory");
+}
+__device__ __forceinline__ unsigned lds_addr(const char* p) {
+    return static_cast<unsigned>(reinterpret_cast<size_t>((const __attribute__((address_space(3))) char*)p));
+}
+
 // bf16 pair {bytes (wa, ba), (wb, bb)} of int8 or e4m3 data: both fit 8
 // significant bits (e4m3: 4), so the high half of the float is the exact bf16;
 // one v_perm_b32 takes both high halves

@@ -84,52 +84,9 @@ __device__ __forceinline__ void wide_mfma_drain(f32x16& s) {
 // Work-group barrier of the pipelined loop: the wave's LDS operations complete,
 // then s_barrier.  Unlike __syncthreads it does not wait for the wave's buffer
 // loads, so the raw tiles in flight to LDS keep streaming through it; a raw tile
-// is waited for explicitly (wide_wait_vm) before the barrier that publishes it.
+// is waited for explicitly (wait_vm) before the barrier that publishes it.
 // The memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void wide_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// wait until at most N of the wave's buffer loads are outstanding
-template <int N>
-__device__ __forceinline__ void wide_wait_vm() {
-    static_assert(N >= 0 && N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
-}
-
-// Buffer load of 4 or 16 bytes a lane straight into LDS at lds + 4 or 16 lane (M0
-// holds lds, one wait state after it is written; restored afterwards).  Written as asm so that the compiler, which cannot
-// tell which LDS bytes such a load writes, does not put a wait for it in front of
-// every later LDS read; the loop waits for its raw tiles itself (wide_wait_vm, then
-// a barrier) before anything reads them.  No VGPR is written.
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4_t raw_rsrc(const void* base, int num_records) {
-    const unsigned long long a = reinterpret_cast<unsigned long long>(base);
-    i32x4_t r;
-    r[0] = static_cast<int>(a & 0xffffffffull);
-    r[1] = static_cast<int>((a >> 32) & 0xffffull);      // stride 0
-    r[2] = num_records;
-    r[3] = 0x00020000;
-    return r;
-}
-template <int BYTES>
-__device__ __forceinline__ void lds_dma(const i32x4_t& rs, unsigned lds, int voff, int soff) {
-    static_assert(BYTES == 4 || BYTES == 16, "dword or dwordx4");
-    int m0_saved;
-    if constexpr (BYTES == 16)
-        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-                     "s_mov_b32 m0, %0"
-                     : "=&s"(m0_saved)
-                     : "s"(lds), "v"(voff), "s"(rs), "s"(soff)
-                     : "memory");
-    else
-        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, %4 offen lds\n\t"
-                     "s_mov_b32 m0, %0"
-                     : "=&s"(m0_saved)
-                     : "s"(lds), "v"(voff), "s"(rs), "s"(soff)
-                     : "memory");
-}
-__device__ __forceinline__ unsigned lds_addr(const char* p) {
-    return static_cast<unsigned>(reinterpret_cast<size_t>((const __attribute__((address_space(3))) char*)p));
-}
-
 // LDS of the pipeline (bytes): K tile [32 keys][D] bf16 in rows padded by 16
 // bytes; V^T tile [4 groups][D dims][8 keys] bf16 followed by the tile's K and V
 // row scales [32] + [32]; raw tile: K [32][D] int8, V [32][D] int8, K scales [64],
@@ -558,7 +515,7 @@ __device__ __forceinline__ void wide_unit(const MParams& p, const int t_split, c
     // prologue: raw tiles 0 and 1 loaded, tile 0 widened
     if (n_tiles > 0) dma_tile(0);
     if (n_tiles > 1) dma_tile(1);
-    wide_wait_vm<0>();
+    wait_vm<0>();
     wide_barrier();                               // raw tiles 0, 1 (and Q^T, paths) in LDS
     if (n_tiles > 0 && wave >= 2) {
         widen_read(0);
@@ -618,7 +575,7 @@ __device__ __forceinline__ void wide_unit(const MParams& p, const int t_split, c
             // full wait, or issued nothing).  Saying so here keeps the compiler, which
             // does not see the raw-tile loads, from placing the wait for a register it
             // reloads before the loop after the raw-tile loads, where they would hold it up.
-            wide_wait_vm<0>();
+            wait_vm<0>();
             if (t + 2 < n_tiles) dma_tile(t + 2);
 
             // ---- phase A: scores of tile t, widening of tile t + 1 ----
@@ -705,7 +662,7 @@ __device__ __forceinline__ void wide_unit(const MParams& p, const int t_split, c
             if constexpr (two) xp1 = x1;
 
             // raw tile t + 2 has landed for every wave before tile t + 1 widens it
-            if (t + 2 < n_tiles) wide_wait_vm<0>();
+            if (t + 2 < n_tiles) wait_vm<0>();
             wide_barrier();                       // tile t + 1 widened; raw buffer t & 1 free
         }
         // the O^T products of the last tile
