@@ -361,8 +361,8 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
     // fills its bytes 1024 c .. 1024 c + 1023, lane l the 16 at 1024 c + 16 l: key
     // (1024 c + 16 l) / D, slot s = ((1024 c + 16 l) mod D) / 16 of the row, which
     // holds 16-byte chunk s ^ ksw(key) of K (s ^ vsw(key) of V) so that the operand
-    // and staging reads below meet no bank conflicts.  Lane l of the two scale loads
-    // takes key l.  2 NRK + 2 loads a tile, all of the wave.
+    // and staging reads below meet no bank conflicts.  Lane l < kLT of the two scale
+    // loads takes key l.  2 NRK + 2 loads a tile, all of the wave.
     constexpr int NRK = kLT * D / 1024;
     constexpr int NDT = 2 * NRK + 2;
     auto ksw = [](int key) { return key & (GCH - 1); };
@@ -387,8 +387,10 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                 lds_dma<16>(krw, lds_addr(raw + 1024 * c), key * cb + ((slot ^ ksw(key)) << 4), t0 * cb);
                 lds_dma<16>(vrw, lds_addr(raw + kLT * D + 1024 * c), key * cb + ((slot ^ vsw(key)) << 4), t0 * cb);
             }
-            lds_dma<4>(ksr, lds_addr(raw + 2 * kLT * D), l * scb, t0 * scb);
-            lds_dma<4>(vsr, lds_addr(raw + 2 * kLT * D + 256), l * scb, t0 * scb);
+            if (l < kLT) {                         // the tile's keys only (interleaved heads)
+                lds_dma<4>(ksr, lds_addr(raw + 2 * kLT * D), l * scb, t0 * scb);
+                lds_dma<4>(vsr, lds_addr(raw + 2 * kLT * D + 256), l * scb, t0 * scb);
+            }
         }
     };
 

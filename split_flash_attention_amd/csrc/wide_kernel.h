@@ -90,7 +90,7 @@ __device__ __forceinline__ void wide_barrier() { asm volatile("s_waitcnt lgkmcnt
 // LDS of the pipeline (bytes): K tile [32 keys][D] bf16 in rows padded by 16
 // bytes; V^T tile [4 groups][D dims][8 keys] bf16 followed by the tile's K and V
 // row scales [32] + [32]; raw tile: K [32][D] int8, V [32][D] int8, K scales [64],
-// V scales [64] (the loads of the scales cover 64 keys; the upper 32 are unused).
+// V scales [64] (slots of 64 keys, of which the loads fill the tile's 32).
 template <int D>
 constexpr int wide_krow() { return D * 2 + 16; }
 template <int D>
@@ -273,7 +273,7 @@ __device__ __forceinline__ void wide_unit(const MParams& p, const int t_split, c
     const i32x4_t srs = raw_rsrc((wave == 0 ? p.ksc : p.vsc) + sc_first, nsc);
     // Wave w loads the 1 KiB pieces w NDMA .. w NDMA + NDMA - 1 of the raw K and V
     // rows (lane l: the 16 bytes at piece offset 16 l, i.e. row (1024 c + 16 l) / D),
-    // wave 0 the K scales and wave 1 the V scales (lane l: key l).  A wave thus has
+    // wave 0 the K scales and wave 1 the V scales (lane l < 32: key l).  A wave thus has
     // 2 NDMA loads in flight per tile, 2 NDMA + 1 for waves 0 and 1.
     auto dma_tile = [&](int t) __attribute__((always_inline)) {
         char* raw = smem + wide_off_raw<D>() + (t & 1) * RBUF;
@@ -289,7 +289,9 @@ __device__ __forceinline__ void wide_unit(const MParams& p, const int t_split, c
             lds_dma<16>(krs, lds_addr(raw + 1024 * c), voff, soff);
             lds_dma<16>(vrs, lds_addr(raw + kWT * D + 1024 * c), voff, soff);
         }
-        if (wave < 2) lds_dma<4>(srs, lds_addr(raw + 2 * kWT * D + wave * 256), ln * scb, t * kWT * scb);
+        // (lanes of keys past the tile load nothing: the scales of the kv heads
+        // interleave, so every extra key would fetch another sector)
+        if (wave < 2 && ln < kWT) lds_dma<4>(srs, lds_addr(raw + 2 * kWT * D + wave * 256), ln * scb, t * kWT * scb);
     };
     // ---- widening raw tile -> K tile (bf16) and V^T tile (bf16) + row scales --------
     // Done by waves 2 and 3 alone (threads wt = tid - 128), which own one block and
