@@ -47,6 +47,48 @@ __device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
 
 // Butterfly exchange within the wave.
 __device__ __forceinline__ float wave_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
+// max(x[l], x[l ^ 32]) and max(x[l], x[l ^ 16]) without a trip through LDS: one
+// v_permlane32_swap / v_permlane16_swap of x with itself leaves each lane holding its
+// own value and its partner's in the two results (in some order); the maximum of
+// the two is the pair's (v_max_f32: a NaN operand gives the other one)
+__device__ __forceinline__ float wave_max_x32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_max_x16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// x[l ^ 32] (x[l ^ 16]) itself: of the two results, the one whose bits differ from
+// the lane's own value (either, when they are equal)
+__device__ __forceinline__ float wave_partner_x32(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0] == u ? r[1] : r[0]);
+}
+__device__ __forceinline__ float wave_partner_x16(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(r[0] == u ? r[1] : r[0]);
+}
+// x[l] + x[l ^ 32] (x[l ^ 16]) and x[l] | x[l ^ 32] (x[l ^ 16]) the same way (addition
+// is commutative, so the sum is the one a lane exchange gives, bit for bit)
+__device__ __forceinline__ float wave_sum_x32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float wave_sum_x16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ int wave_or_x32(int x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
+    return static_cast<int>(r[0] | r[1]);
+}
+__device__ __forceinline__ int wave_or_x16(int x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
+    return static_cast<int>(r[0] | r[1]);
+}
 __device__ __forceinline__ int wave_xor_i(int x, int mask) { return __shfl_xor(x, mask, 64); }
 
 // Lane `src`'s 64-bit value (two 32-bit exchanges).

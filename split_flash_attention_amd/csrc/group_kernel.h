@@ -412,8 +412,8 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
             atomicAdd(my_dbg + 1, sm);
             atomicAdd(my_dbg + 2, sq);
         }
-        tmax = fmaxf(tmax, wave_xor(tmax, 16));
-        tmax = fmaxf(tmax, wave_xor(tmax, 32));
+        tmax = wave_max_x16(tmax);
+        tmax = wave_max_x32(tmax);
         m_true = fmaxf(m_true, tmax);
         const bool need = (tmax > m_use + kLazy) || (m_use == kNegInf && tmax != kNegInf);
         if (wave_any(need)) {
@@ -521,13 +521,13 @@ __device__ __forceinline__ void group_unit(const MParams& p, const int t_split, 
     // ---- epilogue: partials of this slice -------------------------------------
     if (!wave_live) return;
     float l = l_run;
-    l += wave_xor(l, 16);
-    l += wave_xor(l, 32);
+    l = wave_sum_x16(l);
+    l = wave_sum_x32(l);
     {
         // a NaN visible score made this lane's running sum NaN
         int tn = (l_run != l_run) ? 1 : 0;
-        tn |= wave_xor_i(tn, 16);
-        tn |= wave_xor_i(tn, 32);
+        tn = wave_or_x16(tn);
+        tn = wave_or_x32(tn);
         nan_run = tn != 0;
     }
     if (!ok) return;

@@ -785,11 +785,11 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
                 }
             }
             // combine over the four lane groups that hold this query vector
-            tmax = max_keep(tmax, wave_xor(tmax, 16));
-            tmax = max_keep(tmax, wave_xor(tmax, 32));
+            tmax = max_keep(tmax, wave_partner_x16(tmax));
+            tmax = max_keep(tmax, wave_partner_x32(tmax));
             int tn = tnan ? 1 : 0;
-            tn |= wave_xor_i(tn, 16);
-            tn |= wave_xor_i(tn, 32);
+            tn = wave_or_x16(tn);
+            tn = wave_or_x32(tn);
             nan_run[k] = nan_run[k] || tn;
             const float m_new = max_keep(m_run[k], tmax);
             const float c = rescale_factor(m_run[k], m_new);
@@ -870,8 +870,8 @@ __device__ __forceinline__ void attn_unit(const MParams& p, const int t_split, c
 #pragma unroll
     for (int k = 0; k < QB; ++k) {
         float l = l_run[k];
-        l += wave_xor(l, 16);
-        l += wave_xor(l, 32);
+        l = wave_sum_x16(l);
+        l = wave_sum_x32(l);
         long long cnt = 0, sum = 0, sq = 0;
         if (p.dbg_visit) {
             // the four lane groups of a query vector saw disjoint keys: add their counts

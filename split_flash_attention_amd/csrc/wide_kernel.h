@@ -473,7 +473,7 @@ __device__ __forceinline__ void wide_unit(const MParams& p, const int t_split, c
             }
         } else if constexpr (q == 4) {
             float tmax = x.mls;
-            tmax = fmaxf(tmax, wave_xor(tmax, 32));
+            tmax = wave_max_x32(tmax);
             m_true[k] = fmaxf(m_true[k], tmax);
             const bool need = (tmax > m_use[k] + kLazy) || (m_use[k] == kNegInf && tmax != kNegInf);
             // a lane whose reference was still -inf has o = 0 and l = 0: it takes the new
@@ -677,9 +677,9 @@ __device__ __forceinline__ void wide_unit(const MParams& p, const int t_split, c
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         if (!live[k]) continue;                    // uniform
-        float l = l_run[k] + wave_xor(l_run[k], 32);
+        float l = wave_sum_x32(l_run[k]);
         int tn = (l_run[k] != l_run[k]) ? 1 : 0;   // a NaN visible score made a running sum NaN
-        tn |= wave_xor_i(tn, 32);
+        tn = wave_or_x32(tn);
         const bool nan_run = tn != 0;
         unsigned long long cnt = 0, sum = 0, sq = 0;
         if (p.dbg_visit) {

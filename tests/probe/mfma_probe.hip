@@ -136,3 +136,24 @@ extern "C" int lds_dma_probe(const void* src, void* out, void* stream) {
                        static_cast<const uint32_t*>(src), static_cast<uint32_t*>(out));
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
+
+// v_permlane32_swap_b32 and v_permlane16_swap_b32 with both operands holding the
+// same value x: lane l writes the two results of each (out [64][4]: the 32-lane
+// swap's pair, then the 16-lane swap's pair).  The kernels rely on each pair being
+// {x[l], x[l ^ 32]} (resp. {x[l], x[l ^ 16]}) in some order.
+__global__ void __launch_bounds__(64) permlane_swap(const uint32_t* in, uint32_t* out) {
+    const int l = threadIdx.x;
+    const uint32_t x = in[l];
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const auto q = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    out[l * 4 + 0] = r[0];
+    out[l * 4 + 1] = r[1];
+    out[l * 4 + 2] = q[0];
+    out[l * 4 + 3] = q[1];
+}
+
+extern "C" int permlane_probe(const void* in, void* out, void* stream) {
+    hipLaunchKernelGGL(permlane_swap, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint32_t*>(in), static_cast<uint32_t*>(out));
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}

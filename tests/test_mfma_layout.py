@@ -174,3 +174,23 @@ def test_buffer_load_to_lds_places_lane_l_at_16l():
     s = np.arange(1024).reshape(4, 64, 4)           # [wave][16-byte chunk][word]
     want = s[:, ::-1, :].reshape(256, 4)            # lane l of wave w read chunk 63 - l
     assert np.array_equal(o, want)
+
+
+def test_permlane_swaps_pair_each_lane_with_its_partner():
+    """v_permlane32_swap / v_permlane16_swap with both operands x: each lane's two
+    results are x[l] and x[l ^ 32] (x[l ^ 16]) in some order, so their maximum is the
+    two-lane maximum the softmax kernels take with it."""
+    if not torch.cuda.is_available():
+        pytest.fail("needs a GPU")
+    lib = ctypes.CDLL(LIB)
+    x = torch.arange(1000, 1064, dtype=torch.int32, device="cuda")
+    out = torch.full((64, 4), -1, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert lib.permlane_probe(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                              ctypes.c_void_p(st)) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    xs = np.arange(1000, 1064)
+    for l in range(64):
+        assert sorted(o[l, :2]) == sorted([xs[l], xs[l ^ 32]]), (l, o[l])
+        assert sorted(o[l, 2:]) == sorted([xs[l], xs[l ^ 16]]), (l, o[l])
