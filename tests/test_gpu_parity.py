@@ -128,6 +128,15 @@ DECODE_CASES = {
     "fp8_verify_w12_d128_noncausal": dict(n_stream=1, n_row=16, n_head_q=12, n_head_kv=1,
                                           head_dim=128, cap=520, kv_dtype="fp8", depths=[520],
                                           slice_len=512, causal=False),
+    # byte rows on one wave per unit (raw tiles streamed into LDS two tiles ahead,
+    # K widened as read): ragged depths, two-row windows with softcap and ALiBi, trees
+    "i8_gqa8_d256": dict(n_stream=3, n_row=1, n_head_q=32, n_head_kv=4, head_dim=256,
+                         cap=2600, kv_dtype="i8", depths=[1, 1500, 2599], slice_len=1024),
+    "i8_rows2_d128_softcap_alibi": dict(n_stream=2, n_row=2, n_head_q=16, n_head_kv=2, head_dim=128,
+                                        cap=900, kv_dtype="i8", depths=[900, 33], slice_len=256,
+                                        softcap=25.0, alibi=True),
+    "fp8_rows2_d256_tree": dict(n_stream=2, n_row=2, n_head_q=16, n_head_kv=2, head_dim=256,
+                                cap=700, kv_dtype="fp8", depths=[700, 18], slice_len=512, tree="heap"),
     # e4m3 K/V rows with fp32 row scales: one block per unit, and a work-group unit
     "fp8_gqa8_d256": dict(n_stream=2, n_row=1, n_head_q=32, n_head_kv=4, head_dim=256,
                           cap=1800, kv_dtype="fp8", depths=[1800, 700], slice_len=512),
