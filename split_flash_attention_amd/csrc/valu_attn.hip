@@ -25,7 +25,6 @@ constexpr int kTile = 32;       // keys per tile
 constexpr int kQv = 32;         // query vectors per work-group
 constexpr int kThreads = 256;
 constexpr int kMaxD = 256;
-constexpr int kStageU = 8;      // K/V elements per thread in flight while staging a tile
 constexpr int kCombineRound = 8;   // partial slices per lane in flight in the combine
 
 enum Mode : int { kDecode = 0, kMask = 1 };
@@ -126,9 +125,21 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
     };
 
     // ---- load Q, init state ---------------------------------------------
-    for (int e = tid; e < nq * D; e += kThreads) {
-        const int i = e / D, d = e % D;
-        qs[i * kMaxD + d] = qvec_ptr(i)[d];
+    // (float4 pieces, every load of a thread issued before the stores: Q is 16-byte
+    // aligned and D a multiple of 4)
+    {
+        constexpr int NQ4 = kQv * kMaxD / 4 / kThreads;
+        float4 qr[NQ4];
+#pragma unroll
+        for (int u = 0; u < NQ4; ++u) {
+            const int e = (tid + u * kThreads) * 4;
+            if (e < nq * D) qr[u] = *reinterpret_cast<const float4*>(qvec_ptr(e / D) + e % D);
+        }
+#pragma unroll
+        for (int u = 0; u < NQ4; ++u) {
+            const int e = (tid + u * kThreads) * 4;
+            if (e < nq * D) *reinterpret_cast<float4*>(qs + (e / D) * kMaxD + e % D) = qr[u];
+        }
     }
     if (tid < kQv) {
         m_run[tid] = kNegInf;
@@ -202,44 +213,66 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
             __syncthreads();
             continue;
         }
-        // stage K and V of the keys somebody sees: kStageU elements per thread in
-        // flight (all loads of a batch issued before any store), storage type fixed
-        // per instantiation
+        // stage K and V of the keys somebody sees: every 16-byte piece of the tile's
+        // rows this thread takes is loaded at once (one round trip to memory per
+        // tile), then widened to fp32 into LDS; storage type fixed per instantiation.
+        // (The host checks that K, V and their strides are 16-byte aligned.)
         auto stage = [&](auto dt_tag) {
             constexpr int DT = decltype(dt_tag)::value;
-            for (int e0 = tid; e0 < kTile * D; e0 += kThreads * kStageU) {
-                float kx[kStageU], vx[kStageU];
+            constexpr int ES = DT == SEL_ATTN_F32 ? 4 : ((DT == SEL_ATTN_F16 || DT == SEL_ATTN_BF16) ? 2 : 1);
+            constexpr int EPC = 16 / ES;                          // elements per 16-byte piece
+            constexpr int NPC = (kTile * kMaxD / EPC + kThreads - 1) / kThreads;   // pieces per thread
+            const int cpr = D / EPC;                              // pieces per row
+            const int n_pc = kTile * cpr;
+            uint4 kr[NPC], vr[NPC];
+            float ks[NPC], vs[NPC];
 #pragma unroll
-                for (int u = 0; u < kStageU; ++u) {
-                    const int e = e0 + u * kThreads;
-                    kx[u] = 0.f;
-                    vx[u] = 0.f;
-                    if (e < kTile * D) {
-                        const int s = e / D, d = e % D;
-                        const int c = cell_t[s];
-                        if (c >= 0 && ((any >> s) & 1u)) {
-                            const int64_t base = (p.mode == kDecode ? static_cast<int64_t>(b) * p.kv_ss : 0) +
-                                                 static_cast<int64_t>(c) * p.kv_sc +
-                                                 static_cast<int64_t>(g) * p.kv_sh;
-                            kx[u] = load_kv_elem(p.k, base + d, DT);
-                            vx[u] = load_kv_elem(p.v, base + d, DT);
-                            if constexpr (DT == SEL_ATTN_I8 || DT == SEL_ATTN_FP8) {
-                                const int64_t sb = (p.mode == kDecode ? static_cast<int64_t>(b) * p.sc_ss : 0) +
-                                                   static_cast<int64_t>(c) * p.sc_sc +
-                                                   static_cast<int64_t>(g) * p.sc_sh;
-                                kx[u] *= p.ksc[sb];
-                                vx[u] *= p.vsc[sb];
-                            }
+            for (int i = 0; i < NPC; ++i) {
+                const int e = tid + i * kThreads;
+                kr[i] = vr[i] = uint4{0u, 0u, 0u, 0u};
+                ks[i] = vs[i] = 1.f;
+                if (e < n_pc) {
+                    const int s = e / cpr, ch = e % cpr;
+                    const int c = cell_t[s];
+                    if (c >= 0 && ((any >> s) & 1u)) {
+                        const int64_t base = (p.mode == kDecode ? static_cast<int64_t>(b) * p.kv_ss : 0) +
+                                             static_cast<int64_t>(c) * p.kv_sc +
+                                             static_cast<int64_t>(g) * p.kv_sh + static_cast<int64_t>(ch) * EPC;
+                        kr[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(p.k) + base * ES);
+                        vr[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(p.v) + base * ES);
+                        if constexpr (DT == SEL_ATTN_I8 || DT == SEL_ATTN_FP8) {
+                            const int64_t sb = (p.mode == kDecode ? static_cast<int64_t>(b) * p.sc_ss : 0) +
+                                               static_cast<int64_t>(c) * p.sc_sc +
+                                               static_cast<int64_t>(g) * p.sc_sh;
+                            ks[i] = p.ksc[sb];
+                            vs[i] = p.vsc[sb];
                         }
                     }
                 }
+            }
+            // element j of a 16-byte piece as a float (exact widening)
+            auto elem = [](const uint4& w, int j) -> float {
+                const uint32_t x = (j * ES / 4 == 0) ? w.x : (j * ES / 4 == 1) ? w.y : (j * ES / 4 == 2) ? w.z : w.w;
+                if constexpr (DT == SEL_ATTN_F32) return __uint_as_float(x);
+                else if constexpr (DT == SEL_ATTN_BF16) return bf16_to_f32(static_cast<uint16_t>(x >> (16 * (j & 1))));
+                else if constexpr (DT == SEL_ATTN_F16) return f16_to_f32(static_cast<uint16_t>(x >> (16 * (j & 1))));
+                else if constexpr (DT == SEL_ATTN_FP8) return e4m3_to_f32((x >> (8 * (j & 3))) & 0xffu);
+                else return static_cast<float>(static_cast<int8_t>((x >> (8 * (j & 3))) & 0xffu));
+            };
 #pragma unroll
-                for (int u = 0; u < kStageU; ++u) {
-                    const int e = e0 + u * kThreads;
-                    if (e < kTile * D) {
-                        const int s = e / D, d = e % D;
-                        kt[s * (kMaxD + 1) + d] = kx[u];
-                        vt[s * kMaxD + d] = vx[u];
+            for (int i = 0; i < NPC; ++i) {
+                const int e = tid + i * kThreads;
+                if (e < n_pc) {
+                    const int s = e / cpr, d0 = (e % cpr) * EPC;
+#pragma unroll
+                    for (int j = 0; j < EPC; ++j) {
+                        float kx = elem(kr[i], j), vx = elem(vr[i], j);
+                        if constexpr (DT == SEL_ATTN_I8 || DT == SEL_ATTN_FP8) {
+                            kx *= ks[i];
+                            vx *= vs[i];
+                        }
+                        kt[s * (kMaxD + 1) + d0 + j] = kx;
+                        vt[s * kMaxD + d0 + j] = vx;
                     }
                 }
             }
