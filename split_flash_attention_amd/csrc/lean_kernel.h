@@ -593,9 +593,16 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
         if constexpr (RAW) {
             const char* kr = smem + buf * RAWB;
+            // every raw operand read is issued before the first product: left to
+            // itself the scheduler waits for each read right before its product, which
+            // puts one LDS round trip per 32 dims on the tile's critical path
+            uint2 kw[NKK];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) kw[kk] = *reinterpret_cast<const uint2*>(kr + (kraw ^ (kk << 5)));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
-                const uint2 w = *reinterpret_cast<const uint2*>(kr + (kraw ^ (kk << 5)));
+                const uint2 w = kw[kk];
                 const u32x4 a = u32x4{kpair_bf16<KT>(w.x, 0), kpair_bf16<KT>(w.x, 1), kpair_bf16<KT>(w.y, 0),
                                       kpair_bf16<KT>(w.y, 1)};
                 s = mfma16x16x32<F16>(a, qop[kk], s);
