@@ -473,7 +473,7 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
 #pragma unroll
         for (int i = 0; i < NVL; ++i) {
             const int e = lane + 64 * i;
-            if (e < V_TASKS) {
+            if (V_TASKS >= 64 * (i + 1) || e < V_TASKS) {   // (no branch when every lane has a task)
                 int kg, ch;
                 v_task<GCH>(e, kg, ch);
                 if constexpr (B8) {
@@ -520,15 +520,16 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
                 }
             }
         }
-        if constexpr (B8) {
+        if constexpr (RAW) {
+            // (every lane: lanes l, l + 16, l + 32, l + 48 copy the same value, and no
+            // branch splits the scheduling region the staging shares with the products)
+            const int k = lane & (kLT - 1);
+            ksc_lds[k] = reinterpret_cast<const float*>(raw + 2 * kLT * D)[k];
+            vsc_lds[k] = reinterpret_cast<const float*>(raw + 2 * kLT * D + 256)[k];
+        } else if constexpr (B8) {
             if (lane < kLT) {
-                if constexpr (RAW) {
-                    ksc_lds[lane] = reinterpret_cast<const float*>(raw + 2 * kLT * D)[lane];
-                    vsc_lds[lane] = reinterpret_cast<const float*>(raw + 2 * kLT * D + 256)[lane];
-                } else {
-                    ksc_lds[lane] = kscr;
-                    vsc_lds[lane] = vscr;
-                }
+                ksc_lds[lane] = kscr;
+                vsc_lds[lane] = vscr;
             }
         }
         if constexpr (CHK) return mode == 1 && wave_any(nonfinite_found(nfa));
@@ -582,10 +583,18 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
         }
         // uniform: every query vector sees the whole tile
         const bool full = (MODE == kDecode) && t0 + kLT <= n_full;
-        const bool flagged = store_tile(CHK && !full ? 1 : 0, buf);
-        if (flagged) store_tile(2, buf);               // the registers (raw tile) still hold the tile
-        if (t0 + kLT < n_keys) fill_cells(t0 + kLT);
-        __syncthreads();
+        // Byte rows without the non-finite check, one V staging task per lane (RAW1):
+        // the score products read raw K, not the staged V^T, so the tile's V staging
+        // runs between them, one step after each product (the products form one
+        // dependent chain, which would otherwise leave the vector ALU idle).
+        constexpr bool RAW1 = RAW && !CHK && V_TASKS == 64;
+        bool flagged = false;
+        if constexpr (!RAW1) {
+            flagged = store_tile(CHK && !full ? 1 : 0, buf);
+            if (flagged) store_tile(2, buf);           // the registers (raw tile) still hold the tile
+            if (t0 + kLT < n_keys) fill_cells(t0 + kLT);
+            __syncthreads();
+        }
         if constexpr (!RAW) {
             if (t0 + kLT < n_keys) load_tile(t0 + kLT);
         }
@@ -599,13 +608,48 @@ __device__ __forceinline__ void lean_unit(const MParams& p, const int t_split, c
             uint2 kw[NKK];
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) kw[kk] = *reinterpret_cast<const uint2*>(kr + (kraw ^ (kk << 5)));
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (RAW1) {
+                // the lane's V task (keys 4 kg .. 4 kg + 3, chunk ch) and the row scales
+                int kg, ch;
+                v_task<GCH>(lane, kg, ch);
+                u32x4 vw[4];
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const uint2 w = kw[kk];
-                const u32x4 a = u32x4{kpair_bf16<KT>(w.x, 0), kpair_bf16<KT>(w.x, 1), kpair_bf16<KT>(w.y, 0),
-                                      kpair_bf16<KT>(w.y, 1)};
-                s = mfma16x16x32<F16>(a, qop[kk], s);
+                for (int j = 0; j < 4; ++j) {
+                    const int key = 4 * kg + j;
+                    vw[j] = *reinterpret_cast<const u32x4*>(kr + kLT * D + key * D + ((ch ^ vsw(key)) << 4));
+                }
+                const int k = lane & (kLT - 1);         // (lanes l, l + 16, ... copy the same value)
+                ksc_lds[k] = reinterpret_cast<const float*>(kr + 2 * kLT * D)[k];
+                vsc_lds[k] = reinterpret_cast<const float*>(kr + 2 * kLT * D + 256)[k];
+                __builtin_amdgcn_sched_barrier(0);
+                // product kk, then staging steps (dims 2 j, 2 j + 1 of the task's chunk)
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const uint2 w = kw[kk];
+                    const u32x4 a = u32x4{kpair_bf16<KT>(w.x, 0), kpair_bf16<KT>(w.x, 1), kpair_bf16<KT>(w.y, 0),
+                                          kpair_bf16<KT>(w.y, 1)};
+                    s = mfma16x16x32<F16>(a, qop[kk], s);
+#pragma unroll
+                    for (int j = kk * (EPC / 2) / NKK; j < (kk + 1) * (EPC / 2) / NKK; ++j) {
+                        const int dd = 2 * j, wi = dd >> 2, h = (dd >> 1) & 1;
+                        uint32_t lo_e, lo_o, hi_e, hi_o;
+                        vpairs_bf16<KT>(vw[0][wi], vw[1][wi], h, lo_e, lo_o);
+                        vpairs_bf16<KT>(vw[2][wi], vw[3][wi], h, hi_e, hi_o);
+                        *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd, kg)) = uint2{lo_e, hi_e};
+                        *reinterpret_cast<uint2*>(vt_lds + vt16_off(ch * EPC + dd + 1, kg)) = uint2{lo_o, hi_o};
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                __syncthreads();                       // V^T and row scales staged
+            } else {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const uint2 w = kw[kk];
+                    const u32x4 a = u32x4{kpair_bf16<KT>(w.x, 0), kpair_bf16<KT>(w.x, 1), kpair_bf16<KT>(w.y, 0),
+                                          kpair_bf16<KT>(w.y, 1)};
+                    s = mfma16x16x32<F16>(a, qop[kk], s);
+                }
             }
             // the raw tile two ahead goes into this buffer, whose K, V and scales are read
             if (t0 + 2 * kLT < n_keys) dma_tile(t0 + 2 * kLT, buf);
