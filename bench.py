@@ -20,7 +20,8 @@ bytes / 8 TB/s and flops / 2.5 PFLOP/s):
     16/2 heads, 512 block ids per row over 4-cell blocks; 4*D flops per visited
     (row, head, key)) and the selected-key decode (16 rows, one per sequence of a
     unified cache, the key range split 32 ways, then the combine);
-  * the tiny dense decode and the semantic-edge mask prefill;
+  * the tiny dense decode and the semantic-edge mask prefill (its 4096 keys
+    split 8 ways, then the combine; the unsplit call, 64 work-groups, beside it);
   * measured roofs: a 1 GiB device copy (also the calibration of the memory
     counters), a bf16 8192^3 matmul, and a gather probe that reads exactly the
     K/V blocks the selected-key prefill gathers; the selected-key prefill is
@@ -46,6 +47,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 SEL_DECODE_SPLITS = 32         # key-range splits of the selected-key decode rows (16 rows x 2 kv heads each)
+EDGE_SPLITS = 8                # key-range splits of the semantic-edge mask prefill (64 work-groups unsplit)
 
 # HBM bytes of one decode launch on the split-K workload, from two rocprofv3 --pmc
 # runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
@@ -53,9 +55,9 @@ SEL_DECODE_SPLITS = 32         # key-range splits of the selected-key decode row
 # the copied bytes: factor 2.0; WRITE_SIZE reads them all: factor 1.0).  The
 # figures describe the decode kernel's sources as they were when measured (the
 # SHA-256 below); once those change they are stale and `traffic` is null.
-DECODE_TRAFFIC = {"sources_sha256": "63ef3d399f110de57cce53d2ccce9a534760bcfa9cf4f990c5a08337aef7799f",
-                  "fetch_bytes": 592477.0 * 1024 * 2.0,
-                  "write_bytes": 9702.56 * 1024 * 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "9171308961193aa1199184c6538e093e1f74dd98c3990148db33db6bf70c564b",
+                  "fetch_bytes": 592472.0 * 1024 * 2.0,
+                  "write_bytes": 9702.48 * 1024 * 1.0}
 # the files the decode kernel is built from
 DECODE_SOURCES = ["arch.h", "common.h", "device_cache.h", "internal.h", "mfma_kernel.h", "lean_kernel.h", "mfma_decode.hip"]
 
@@ -571,15 +573,30 @@ def main():
                                    "us_median": round(c1_med * 1e3, 2), "us_min": round(c1_min * 1e3, 2)}
     small4 = {}
     for name, wl4 in (("4", gen.config4()), ("4c", gen.config4(nan=False))):
-        d4 = hip_run.PrefillDev(wl4, "cuda", poison_outputs=False)
-        a4 = d4.args()
-        sa.sel_attn_prefill(a4)
-        small4[name] = timed_each(lambda: sa.sel_attn_prefill(a4), args.steps, torch)
+        # the timed launch: 8 key-range splits (512 work-groups), then the combine
+        d4 = hip_run.PrefillDev(wl4, "cuda", n_splits=EDGE_SPLITS, poison_outputs=False)
+        a4, c4 = d4.args(), sa.combine_args(part_o=d4.part_o, part_ml=d4.part_ml,
+                                            out=d4.out.view(1, *d4.out.shape), sinks=d4.sinks)
+
+        def step4():
+            sa.sel_attn_prefill(a4)
+            sa.sel_attn_split_combine(c4)
+
+        settle(step4, args.warmup, torch)
+        small4[name] = timed_each(step4, args.steps, torch)
         del d4
+        if name == "4":
+            d4u = hip_run.PrefillDev(wl4, "cuda", poison_outputs=False)
+            a4u = d4u.args()
+            sa.sel_attn_prefill(a4u)
+            small4["4u"] = timed_each(lambda: sa.sel_attn_prefill(a4u), args.steps, torch)
+            del d4u
     result["semantic_edge_prefill"] = {"workload": "256 rows x 4096 keys, 16/4 heads, D=128, fp16, softcap, "
-                                                   "ALiBi, F32 mask (with NaN K / control without)",
+                                                   f"ALiBi, F32 mask (with NaN K / control without), "
+                                                   f"{EDGE_SPLITS} key-range splits + combine",
                                        "us_median": round(small4["4"][0] * 1e3, 2),
-                                       "us_median_control": round(small4["4c"][0] * 1e3, 2)}
+                                       "us_median_control": round(small4["4c"][0] * 1e3, 2),
+                                       "us_median_unsplit": round(small4["4u"][0] * 1e3, 2)}
     copy_src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")     # 1 GiB
     copy_dst = torch.empty_like(copy_src)
     copy_src.fill_(1.0)

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import bench
 import oracle
 from tests import hip_run
 from tests.test_gpu_parity import TOL, nmse_check
@@ -101,12 +102,15 @@ def test_config3_selected_key_prefill_full():
 
 
 @pytest.mark.parametrize("nan", [True, False])
-def test_config4_semantic_edge_prefill_full(nan):
+@pytest.mark.parametrize("n_splits", [1, bench.EDGE_SPLITS])
+def test_config4_semantic_edge_prefill_full(nan, n_splits):
+    """Both the unsplit call and the launch bench.py times (key-range splits, then
+    the combine) against the oracle."""
     wl = gen.config4(nan=nan)
-    out = hip_run.run_prefill(wl)
+    out = hip_run.run_prefill(wl, n_splits=n_splits)
     ref = oracle.prefill(q=wl.q, k=wl.k, v=wl.v, kv_dtype="f16", scale=wl.scale, softcap=wl.softcap,
                          alibi=wl.alibi, q_pos=wl.q_pos, mask=wl.mask, causal=True)
-    nmse_check(out, ref, TOL["f16"], f"config4 nan={nan}")
+    nmse_check(out, ref, TOL["f16"], f"config4 nan={nan} splits={n_splits}")
     ex = wl.meta["excluded_rows"]
     assert ex.size == 8
     assert np.all(out[ex] == 0) and not np.signbit(out[ex]).any()
@@ -120,7 +124,6 @@ def test_config4_semantic_edge_prefill_full(nan):
 def test_selected_key_decode_full():
     """The selected-key decode workload in the launch configuration bench.py times
     (32 key-range splits + combine), against the oracle on every row."""
-    import bench
     wl = gen.sel_decode()
     out = hip_run.run_prefill(wl, n_splits=bench.SEL_DECODE_SPLITS)
     assert np.isfinite(out).all()
