@@ -23,7 +23,8 @@ bytes / 8 TB/s and flops / 2.5 PFLOP/s):
   * the tiny dense decode and the semantic-edge mask prefill (its 4096 keys
     split 8 ways, then the combine; the unsplit call, 64 work-groups, beside it);
   * measured roofs: a 1 GiB device copy (also the calibration of the memory
-    counters), a bf16 8192^3 matmul, and a gather probe that reads exactly the
+    counters), a bf16 8192^3 matmul, the issue rate of the two bf16 matrix-core
+    product shapes the kernels use, and a gather probe that reads exactly the
     K/V blocks the selected-key prefill gathers; the selected-key prefill is
     also timed right after a 512 MiB write (cold Infinity Cache).
 Then the FP64 oracle is timed on the host cores on bounded samples of the
@@ -416,6 +417,35 @@ def memory_roofs(torch):
     return res
 
 
+def mfma_rates(torch):
+    """Issue rate of the two bf16 matrix-core shapes the kernels use, from the MFMA
+    probe: 256 work-groups of one wave per SIMD, 4 independent accumulator chains
+    (throughput) and 1 chain (a dependent chain, as in a tile's score products).
+    Returns {shape: {chains: (TFLOP/s over the chip, core cycles per product)}}."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "tests", "probe", "libmfma_probe.so"))
+    lib.mfma_rate_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    groups, iters = 256, 4096
+    out = torch.empty(groups * 256, dtype=torch.float32, device="cuda")
+    ticks = torch.empty(groups, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for shape, name, flop in ((32, "32x32x16_bf16", 32768.0), (16, "16x16x32_bf16", 16384.0)):
+        res[name] = {}
+        for chains in (4, 1):
+            def run():
+                rc = lib.mfma_rate_probe(shape, chains, iters, groups, out.data_ptr(), ticks.data_ptr(), stream)
+                assert rc == 0, rc
+            run()
+            ms = timed_each(run, 5, torch)[0]
+            torch.cuda.synchronize()
+            cyc = float(ticks.double().median().item()) / (iters * chains)
+            tflops = groups * 4 * iters * chains * flop / (ms * 1e-3) / 1e12
+            res[name][f"chains_{chains}"] = {"tflops": round(tflops, 1), "cycles_per_product": round(cyc, 2)}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -613,7 +643,8 @@ def main():
     result["roofs"] = {"hbm_peak_gbs": HBM_PEAK_GBS, "bf16_mfma_peak_tflops": BF16_PEAK_TFLOPS,
                        "copy_gbs": round(copy_gbs, 1),
                        "bf16_matmul_tflops": round(2.0 * 8192 ** 3 / (ms_mm * 1e-3) / 1e12, 1),
-                       "sel_gather_gbs": result["sel_prefill"]["gather_roof_gbs"]}
+                       "sel_gather_gbs": result["sel_prefill"]["gather_roof_gbs"],
+                       "mfma_rates": mfma_rates(torch)}
     result["copy_gbs"] = round(copy_gbs, 1)
 
     if not args.no_cpu_baseline:

@@ -157,3 +157,54 @@ extern "C" int permlane_probe(const void* in, void* out, void* stream) {
                        static_cast<const uint32_t*>(in), static_cast<uint32_t*>(out));
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
+
+// Matrix-core issue rate: `groups` work-groups of four waves (one per SIMD), each
+// wave running `iters` rounds of C independent accumulator chains of one product
+// shape (16: v_mfma_f32_16x16x32_bf16, 32: v_mfma_f32_32x32x16_bf16).  Wave 0 of
+// each work-group writes the s_memtime ticks of its loop to ticks[group] (core clock
+// cycles); every lane writes a sum of its accumulators to out[group * 256 + lane] so
+// the products are not removed.  Buffers: out [groups][256] float, ticks [groups].
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+template <int SHAPE, int C>
+__global__ void __launch_bounds__(256, 1) mfma_rate(float* out, long long* ticks, int iters) {
+    bf16x8_t a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = static_cast<__bf16>(0.001f * static_cast<float>((threadIdx.x + i) & 15));
+        b[i] = static_cast<__bf16>(0.002f * static_cast<float>(i));
+    }
+    f32x4 c[C];
+    f32x16 d[C];
+    for (int j = 0; j < C; ++j) {
+        c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 16; ++e) d[j][e] = 0.f;
+    }
+    const long long t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            if constexpr (SHAPE == 16) c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[j], 0, 0, 0);
+            else d[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d[j], 0, 0, 0);
+        }
+    }
+    const long long t1 = __builtin_amdgcn_s_memtime();
+    float s = 0.f;
+    for (int j = 0; j < C; ++j) {
+        for (int e = 0; e < 4; ++e) s += c[j][e];
+        for (int e = 0; e < 16; ++e) s += d[j][e];
+    }
+    out[blockIdx.x * 256 + threadIdx.x] = s;
+    if (threadIdx.x == 0) ticks[blockIdx.x] = t1 - t0;
+}
+
+extern "C" int mfma_rate_probe(int shape, int chains, int iters, int groups, void* out, void* ticks, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float* o = static_cast<float*>(out);
+    long long* t = static_cast<long long*>(ticks);
+    if (groups <= 0 || iters <= 0) return -1;
+    if (shape == 16 && chains == 1) hipLaunchKernelGGL((mfma_rate<16, 1>), dim3(groups), dim3(256), 0, st, o, t, iters);
+    else if (shape == 16 && chains == 4) hipLaunchKernelGGL((mfma_rate<16, 4>), dim3(groups), dim3(256), 0, st, o, t, iters);
+    else if (shape == 32 && chains == 1) hipLaunchKernelGGL((mfma_rate<32, 1>), dim3(groups), dim3(256), 0, st, o, t, iters);
+    else if (shape == 32 && chains == 4) hipLaunchKernelGGL((mfma_rate<32, 4>), dim3(groups), dim3(256), 0, st, o, t, iters);
+    else return -1;
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
