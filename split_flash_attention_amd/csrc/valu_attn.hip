@@ -64,8 +64,11 @@ struct ValuParams {
 
 // LDS carve-up (bytes)
 constexpr int kOffQ = 0;                                         // float [kQv][kMaxD]
-constexpr int kOffK = kOffQ + kQv * kMaxD * 4;                   // float [kTile][kMaxD+1]
-constexpr int kOffV = kOffK + kTile * (kMaxD + 1) * 4;           // float [kTile][kMaxD]
+// K rows are padded by 4 floats: 16-byte aligned for float4 reads, and the 16 rows one
+// such read of a half-wave touches start on distinct bank groups
+constexpr int kKs = kMaxD + 4;                                   // K row stride (floats)
+constexpr int kOffK = kOffQ + kQv * kMaxD * 4;                   // float [kTile][kKs]
+constexpr int kOffV = kOffK + kTile * kKs * 4;                   // float [kTile][kMaxD]
 constexpr int kOffP = kOffV + kTile * kMaxD * 4;                 // float [kQv][kTile]
 constexpr int kSmemBytes = kOffP + kQv * kTile * 4;
 
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
                             kx *= ks[i];
                             vx *= vs[i];
                         }
-                        kt[s * (kMaxD + 1) + d0 + j] = kx;
+                        kt[s * kKs + d0 + j] = kx;
                         vt[s * kMaxD + d0 + j] = vx;
                     }
                 }
@@ -289,16 +292,19 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
         for (int e = tid; e < kQv * kTile; e += kThreads) {
             const int i = e / kTile, s = e % kTile;
             if (i >= nq || !((vis[i] >> s) & 1u)) continue;
-            // four partial sums (D is a multiple of 4), so the multiply-adds overlap
+            // four partial sums (D is a multiple of 4), so the multiply-adds overlap;
+            // Q and K read four floats at a time
             float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
             const float* qi = qs + i * kMaxD;
-            const float* ks = kt + s * (kMaxD + 1);
+            const float* ks = kt + s * kKs;
 #pragma unroll 4
             for (int d = 0; d < D; d += 4) {
-                d0 = fmaf(qi[d], ks[d], d0);
-                d1 = fmaf(qi[d + 1], ks[d + 1], d1);
-                d2 = fmaf(qi[d + 2], ks[d + 2], d2);
-                d3 = fmaf(qi[d + 3], ks[d + 3], d3);
+                const float4 q4 = *reinterpret_cast<const float4*>(qi + d);
+                const float4 k4 = *reinterpret_cast<const float4*>(ks + d);
+                d0 = fmaf(q4.x, k4.x, d0);
+                d1 = fmaf(q4.y, k4.y, d1);
+                d2 = fmaf(q4.z, k4.z, d2);
+                d3 = fmaf(q4.w, k4.w, d3);
             }
             const float dot = (d0 + d1) + (d2 + d3);
             const int c = cell_t[s];
@@ -367,10 +373,11 @@ __global__ __launch_bounds__(kThreads) void valu_attn_kernel(ValuParams p) {
                 float a0 = acc[u] * c_run[i], a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
                 for (int s = 0; s < kTile; s += 4) {
-                    if ((bits >> s) & 1u) a0 = fmaf(ps[i * kTile + s], vt[s * kMaxD + d_own], a0);
-                    if ((bits >> (s + 1)) & 1u) a1 = fmaf(ps[i * kTile + s + 1], vt[(s + 1) * kMaxD + d_own], a1);
-                    if ((bits >> (s + 2)) & 1u) a2 = fmaf(ps[i * kTile + s + 2], vt[(s + 2) * kMaxD + d_own], a2);
-                    if ((bits >> (s + 3)) & 1u) a3 = fmaf(ps[i * kTile + s + 3], vt[(s + 3) * kMaxD + d_own], a3);
+                    const float4 p4 = *reinterpret_cast<const float4*>(ps + i * kTile + s);   // (one read, broadcast)
+                    if ((bits >> s) & 1u) a0 = fmaf(p4.x, vt[s * kMaxD + d_own], a0);
+                    if ((bits >> (s + 1)) & 1u) a1 = fmaf(p4.y, vt[(s + 1) * kMaxD + d_own], a1);
+                    if ((bits >> (s + 2)) & 1u) a2 = fmaf(p4.z, vt[(s + 2) * kMaxD + d_own], a2);
+                    if ((bits >> (s + 3)) & 1u) a3 = fmaf(p4.w, vt[(s + 3) * kMaxD + d_own], a3);
                 }
                 acc[u] = (a0 + a1) + (a2 + a3);
             }
