@@ -225,9 +225,11 @@ __device__ __forceinline__ uint32_t kpair_bf16(uint32_t w, int h) {
 template <int KT>
 __device__ __forceinline__ void vpairs_bf16(uint32_t wa, uint32_t wb, int h, uint32_t& even, uint32_t& odd) {
     if constexpr (KT == SEL_ATTN_FP8) {
-        const uint32_t pa = fp8_pk_bf16(wa, h != 0), pb = fp8_pk_bf16(wb, h != 0);
-        even = __builtin_amdgcn_perm(pb, pa, 0x05040100u);
-        odd = __builtin_amdgcn_perm(pb, pa, 0x07060302u);
+        // bytes 2h, 2h + 1 of a and b interleaved as {a 2h, b 2h, a 2h+1, b 2h+1}, then one
+        // pair convert per half: three instructions for the four values
+        const uint32_t t = __builtin_amdgcn_perm(wb, wa, h != 0 ? 0x07030602u : 0x05010400u);
+        even = fp8_pk_bf16(t, false);
+        odd = fp8_pk_bf16(t, true);
     } else {
         even = bpair_bf16<KT>(wa, 2 * h, wb, 2 * h);
         odd = bpair_bf16<KT>(wa, 2 * h + 1, wb, 2 * h + 1);
